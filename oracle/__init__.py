@@ -1,0 +1,163 @@
+"""CPU oracle for ragged-dot.  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, the smoke check and the benchmark's CPU-baseline leg may import this
+package.  It shares no code with the GPU library (``group_gemm_amd``) and never imports
+it.  The arithmetic lives in ``oracle.c`` (fp64 accumulation); this module marshals
+numpy arrays into it and adds the padded-dot procedure, written with numpy in fp64.
+
+Sources: "Group-GEMM in XLA: Making Mixture-of-Experts Fast and Memory-Efficient"
+(AMD ROCm blog) -- Part 1 "The Ragged-Dot Operation" and "The Naive Support, and Why It
+Hurts: Padded-Dot"; Part 3 "Non-Contracting (the MoE Case)" and "Contracting".
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+F32, BF16, E4M3 = 0, 1, 2          # the oracle's own element codes (see oracle.c)
+
+_lib = None
+
+
+def lib():
+    """Load liboracle.so, compiling it first if it is not there yet."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.oracle_ragged_dot_m.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, i32,
+                                          vp, i64, vp]
+        L.oracle_ragged_dot_m.restype = ctypes.c_int
+        L.oracle_ragged_dot_k.argtypes = [ctypes.c_int, vp, vp, vp, i64, i64, i64, i32, vp, i64,
+                                          vp]
+        L.oracle_ragged_dot_k.restype = ctypes.c_int
+        for name in ("orc_decode_bf16", "orc_decode_e4m3", "orc_decode_e8m0"):
+            getattr(L, name).restype = ctypes.c_double
+        L.orc_decode_bf16.argtypes = [ctypes.c_uint16]
+        L.orc_decode_e4m3.argtypes = [ctypes.c_uint8]
+        L.orc_decode_e8m0.argtypes = [ctypes.c_uint8]
+        L.oracle_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(a):
+    """Element code of a raw input array: float32 -> F32, uint16 (bf16 bits) -> BF16,
+    uint8 (e4m3 codes) -> E4M3."""
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.uint8:
+        return E4M3
+    raise TypeError(f"unsupported oracle input dtype {a.dtype}")
+
+
+def ragged_dot_m(lhs, rhs, group_sizes, lhs_scale=None, rhs_scale=None, rows=None):
+    """fp64 result of the non-contracting ragged dot: [m, n], or only the listed rows.
+
+    lhs [m, k] and rhs [g, k, n] are float32, uint16 (bfloat16 bit patterns) or uint8 (OCP
+    e4m3 codes, then with E8M0 ``lhs_scale`` [m, k/32] and ``rhs_scale`` [g, k/32, n]).
+    """
+    lhs = np.ascontiguousarray(lhs)
+    rhs = np.ascontiguousarray(rhs)
+    gs = np.ascontiguousarray(group_sizes, dtype=np.int32)
+    m, k = lhs.shape
+    g, k2, n = rhs.shape
+    assert k2 == k and gs.shape == (g,) and lhs.dtype == rhs.dtype
+    code = _dtype_code(lhs)
+    if code == E4M3:
+        lhs_scale = np.ascontiguousarray(lhs_scale, dtype=np.uint8)
+        rhs_scale = np.ascontiguousarray(rhs_scale, dtype=np.uint8)
+        assert lhs_scale.shape == (m, k // 32) and rhs_scale.shape == (g, k // 32, n)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = m if rows is None else rows.shape[0]
+    out = np.empty((nrows, n), dtype=np.float64)
+    rc = lib().oracle_ragged_dot_m(code, _ptr(lhs), _ptr(rhs), _ptr(lhs_scale), _ptr(rhs_scale),
+                                   _ptr(gs), m, k, n, g, _ptr(rows), nrows, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_ragged_dot_m rejected its arguments")
+    return out
+
+
+def ragged_dot_k(lhs, dout, group_sizes, pairs=None):
+    """fp64 result of the contracting ragged dot: [g, k, n], or the rows out[g_q, i_q, :]
+    for the (g, i) pairs given as an int array of shape [npairs, 2]."""
+    lhs = np.ascontiguousarray(lhs)
+    dout = np.ascontiguousarray(dout)
+    gs = np.ascontiguousarray(group_sizes, dtype=np.int32)
+    m, k = lhs.shape
+    m2, n = dout.shape
+    assert m2 == m and lhs.dtype == dout.dtype
+    g = gs.shape[0]
+    code = _dtype_code(lhs)
+    if pairs is not None:
+        pairs = np.ascontiguousarray(pairs, dtype=np.int64).reshape(-1, 2)
+    npairs = g * k if pairs is None else pairs.shape[0]
+    out = np.empty((npairs, n), dtype=np.float64)
+    rc = lib().oracle_ragged_dot_k(code, _ptr(lhs), _ptr(dout), _ptr(gs), m, k, n, g,
+                                   _ptr(pairs), npairs, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_ragged_dot_k rejected its arguments")
+    return out.reshape(g, k, n) if pairs is None else out
+
+
+def decode(a, scale=None, scale_axis=None):
+    """fp64 values of raw inputs via the oracle's own decoders (elementwise calls; meant
+    for small arrays).  For e4m3 codes pass the E8M0 ``scale`` array and the axis along
+    which one scale covers 32 elements."""
+    L = lib()
+    a = np.asarray(a)
+    code = _dtype_code(a)
+    if code == F32:
+        v = a.astype(np.float64)
+    elif code == BF16:
+        v = np.vectorize(L.orc_decode_bf16, otypes=[np.float64])(a)
+    else:
+        v = np.vectorize(L.orc_decode_e4m3, otypes=[np.float64])(a)
+    if scale is not None:
+        s = np.vectorize(L.orc_decode_e8m0, otypes=[np.float64])(np.asarray(scale))
+        v = v * np.repeat(s, 32, axis=scale_axis)
+    return v
+
+
+def padded_dot_m(lhs, rhs, group_sizes, capacity, lhs_scale=None, rhs_scale=None):
+    """The padded-dot baseline written as its three steps, in fp64 numpy:
+    (1) scatter group g's rows into slab P[g, 0:m_g] of a zeroed [g, C, k] buffer;
+    (2) one batched matmul P[g] @ rhs[g] -> [g, C, n];
+    (3) gather rows 0:m_g of every slab back into the [m, n] output.
+    Rows past a group's capacity are dropped (they read as 0), as are rows past
+    sum(group_sizes) -- the same clamping reading as the ragged oracle.
+    ("Group-GEMM in XLA", Part 1 "The Naive Support, and Why It Hurts: Padded-Dot".)"""
+    gs = np.asarray(group_sizes, dtype=np.int64)
+    m, k = lhs.shape
+    g, _, n = rhs.shape
+    A = decode(lhs, lhs_scale, 1) if lhs_scale is not None else decode(lhs)
+    B = decode(rhs, rhs_scale, 1) if rhs_scale is not None else decode(rhs)
+    P = np.zeros((g, capacity, k))
+    start, covered = [], 0
+    for h in range(g):
+        s = min(max(int(gs[h]), 0), m - covered)
+        start.append((covered, s))
+        c = min(s, capacity)
+        P[h, :c] = A[covered:covered + c]
+        covered += s
+    Q = np.matmul(P, B)                      # step 2: uniform batched GEMM
+    out = np.zeros((m, n))
+    for h, (st, s) in enumerate(start):
+        c = min(s, capacity)
+        out[st:st + c] = Q[h, :c]
+    return out
+
+
+def num_threads():
+    return lib().oracle_num_threads()
