@@ -1,0 +1,166 @@
+"""ctypes binding of libgroupgemm.so: argument marshalling only.
+
+Every computation happens in the library's HIP kernels.  torch supplies device memory
+and the current stream; there is no CPU fallback: if the library is missing or a call
+fails, an exception is raised.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgroupgemm.so")
+
+GG_DT = {torch.float32: 0, torch.bfloat16: 1, torch.uint8: 2, torch.float8_e4m3fn: 2}
+OP = {"ragged_m": 0, "ragged_k": 1, "padded_m": 2, "padded_k": 3}
+DEV_NEGATIVE_SIZE, DEV_SUM_EXCEEDS_M, DEV_OVER_CAPACITY = 0x1, 0x2, 0x4
+
+_lib = None
+
+
+class GGError(RuntimeError):
+    def __init__(self, code, what):
+        super().__init__(f"{what}: {status_string(code)} (code {code})")
+        self.code = code
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m group_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        L.gg_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i32, i64, ctypes.c_int]
+        L.gg_workspace_bytes.restype = sz
+        L.ragged_dot_m.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
+        L.ragged_dot_k.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, ctypes.c_int, vp, sz, vp]
+        L.padded_dot.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i32, i64, ctypes.c_int, ctypes.c_int,
+                                 vp, vp, vp, sz, vp]
+        L.gg_schedule.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
+        L.gg_read_device_status.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
+        L.gg_status_string.argtypes = [ctypes.c_int]
+        L.gg_status_string.restype = ctypes.c_char_p
+        L.gg_abi_version.restype = ctypes.c_int
+        for f in ("ragged_dot_m", "ragged_dot_k", "padded_dot", "gg_schedule", "gg_read_device_status"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(code):
+    return lib().gg_status_string(code).decode()
+
+
+def abi_version():
+    return lib().gg_abi_version()
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(code, what):
+    if code != 0:
+        raise GGError(code, what)
+
+
+def workspace_bytes(op, m, k, n, g, capacity=0, in_dtype=torch.bfloat16):
+    return int(lib().gg_workspace_bytes(OP[op], m, k, n, g, capacity, GG_DT[in_dtype]))
+
+
+def _workspace(op, m, k, n, g, capacity, in_dtype, device, workspace):
+    need = workspace_bytes(op, m, k, n, g, capacity, in_dtype)
+    if need == 0:
+        raise ValueError("bad arguments for the workspace size")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def ragged_dot_m(lhs, rhs, group_sizes, out=None, out_dtype=None, lhs_scale=None, rhs_scale=None, workspace=None):
+    """out[m,n]: row block of group h of lhs [m,k] times rhs[h] [k,n]; rows past
+    sum(group_sizes) are 0.  e4m3 inputs (uint8 codes) need E8M0 lhs_scale [m,k/32] and
+    rhs_scale [g,k/32,n]."""
+    m, k = lhs.shape
+    g, k2, n = rhs.shape
+    if k2 != k or group_sizes.shape != (g,) or group_sizes.dtype != torch.int32:
+        raise ValueError("shape/dtype mismatch")
+    if out_dtype is None:
+        out_dtype = torch.float32 if lhs.dtype == torch.float32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=lhs.device)
+    ws = _workspace("ragged_m", m, k, n, g, 0, lhs.dtype, lhs.device, workspace)
+    code = lib().ragged_dot_m(_p(lhs), _p(rhs), _p(group_sizes), _p(out), m, k, n, g, GG_DT[lhs.dtype],
+                              GG_DT[out.dtype], _p(lhs_scale), _p(rhs_scale), _p(ws), ws.numel(),
+                              _stream(lhs.device))
+    _check(code, "ragged_dot_m")
+    return out
+
+
+def ragged_dot_k(lhs, dout, group_sizes, out=None, out_dtype=torch.float32, workspace=None):
+    """out[g,k,n]: out[h] = lhs[rows of h]^T . dout[rows of h]; empty groups give 0."""
+    m, k = lhs.shape
+    m2, n = dout.shape
+    g = group_sizes.shape[0]
+    if m2 != m or group_sizes.dtype != torch.int32:
+        raise ValueError("shape/dtype mismatch")
+    if out is None:
+        out = torch.empty((g, k, n), dtype=out_dtype, device=lhs.device)
+    ws = _workspace("ragged_k", m, k, n, g, 0, lhs.dtype, lhs.device, workspace)
+    code = lib().ragged_dot_k(_p(lhs), _p(dout), _p(group_sizes), _p(out), m, k, n, g, GG_DT[lhs.dtype],
+                              GG_DT[out.dtype], _p(ws), ws.numel(), _stream(lhs.device))
+    _check(code, "ragged_dot_k")
+    return out
+
+
+def padded_dot(mode, a, b, group_sizes, capacity, out=None, out_dtype=None, a_scale=None, b_scale=None,
+               workspace=None):
+    """The capacity-padded baseline: mode "m" (a = lhs, b = rhs) or "k" (a = lhs, b = dout)."""
+    g = group_sizes.shape[0]
+    m, k = a.shape
+    if mode == "m":
+        n = b.shape[2]
+        shape = (m, n)
+        if out_dtype is None:
+            out_dtype = torch.float32 if a.dtype == torch.float32 else torch.bfloat16
+    else:
+        n = b.shape[1]
+        shape = (g, k, n)
+        if out_dtype is None:
+            out_dtype = torch.float32
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=a.device)
+    op = "padded_" + mode
+    ws = _workspace(op, m, k, n, g, capacity, a.dtype, a.device, workspace)
+    code = lib().padded_dot(OP[op], _p(a), _p(b), _p(group_sizes), _p(out), m, k, n, g, capacity, GG_DT[a.dtype],
+                            GG_DT[out.dtype], _p(a_scale), _p(b_scale), _p(ws), ws.numel(), _stream(a.device))
+    _check(code, "padded_dot")
+    return out
+
+
+def build_schedule(group_sizes, m, n, block_m, block_n):
+    """Run the scan alone; returns (row_off int32[g+1], tile_off int32[g+1], status) on
+    the device."""
+    g = group_sizes.shape[0]
+    dev = group_sizes.device
+    row_off = torch.empty(g + 1, dtype=torch.int32, device=dev)
+    tile_off = torch.empty(g + 1, dtype=torch.int32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    code = lib().gg_schedule(_p(group_sizes), m, n, g, block_m, block_n, _p(row_off), _p(tile_off), _p(status),
+                             _stream(dev))
+    _check(code, "gg_schedule")
+    return row_off, tile_off, status
+
+
+def read_device_status(workspace):
+    flags = ctypes.c_uint32(0)
+    _check(lib().gg_read_device_status(_p(workspace), ctypes.byref(flags), _stream(workspace.device)),
+           "gg_read_device_status")
+    return flags.value

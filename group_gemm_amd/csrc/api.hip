@@ -1,0 +1,270 @@
+// api.hip -- the C ABI: argument validation, workspace layout, grid sizing and launches.
+// Host code only; it never reads group_sizes or any other device data (except in
+// gg_read_device_status, which exists for tests), never synchronises and never allocates,
+// so every call can be captured in a HIP graph.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "groupgemm.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr size_t kHeader = 256;   // workspace bytes before any padded buffer (status word first)
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t elem_bytes(gg_dtype d) { return d == GG_DT_F32 ? 4 : d == GG_DT_BF16 ? 2 : 1; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compute units of the current device, cached per device.
+int device_cus(int* cus) {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) { *cus = cache[dev]; return 0; }
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return -1;
+    if (dev >= 0 && dev < 64) cache[dev] = v;
+    *cus = v;
+    return 0;
+}
+
+// Persistent grid: one workgroup per CU (the big-tile kernels hold 128+ KiB of LDS),
+// never more than there are tiles, at least 1 so the status word is always written.
+int persistent_grid(int64_t tile_bound, int per_cu, int cus) {
+    int64_t g = (int64_t)cus * per_cu;
+    if (tile_bound < g) g = tile_bound;
+    if (g < 1) g = 1;
+    return (int)g;
+}
+
+bool fits_i32(int64_t x) { return x >= 0 && x <= INT32_MAX; }
+
+gg_status check_common(int64_t m, int64_t k, int64_t n, int32_t g, const int32_t* gs, void* ws, size_t ws_bytes,
+                       size_t need) {
+    if (!gs || !ws) return GG_ERR_NULL_PTR;
+    if (m < 0 || k < 0 || n < 0 || g < 1 || g > GG_MAX_GROUPS) return GG_ERR_BAD_SHAPE;
+    if (!fits_i32(m) || !fits_i32(k) || !fits_i32(n)) return GG_ERR_BAD_SHAPE;
+    if (!aligned(ws, 16) || !aligned(gs, 4)) return GG_ERR_MISALIGNED;
+    if (ws_bytes < need) return GG_ERR_WORKSPACE_TOO_SMALL;
+    return GG_OK;
+}
+
+// ragged_dot_m body, shared with the batched stage of padded_dot (uniform_rows > 0).
+gg_status run_m(const void* lhs, const void* rhs, const int32_t* gs, void* out, int64_t m, int64_t k, int64_t n,
+                int32_t g, gg_dtype in, gg_dtype outd, const uint8_t* ls, const uint8_t* rs, uint32_t* status,
+                int uniform_rows, hipStream_t s) {
+    int cus;
+    if (device_cus(&cus) != 0) return GG_ERR_HIP;
+    gg::MParams p{};
+    p.lhs = lhs; p.rhs = rhs; p.lhs_scale = ls; p.rhs_scale = rs; p.group_sizes = gs; p.out = out; p.status = status;
+    p.m = (int)m; p.k = (int)k; p.n = (int)n; p.g = g; p.uniform_rows = uniform_rows;
+    p.out_f32 = outd == GG_DT_F32;
+    hipError_t e;
+    if (in == GG_DT_F32) {
+        gg::TileShape ts = gg::tiles_m_f32();
+        int64_t bound = (cdiv64(m, ts.bm) + g + 1) * cdiv64(n, ts.bn);
+        if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
+        e = gg::launch_ragged_m_f32(p, persistent_grid(bound, 4, cus), s);
+    } else if (in == GG_DT_BF16) {
+        gg::TileShape ts = gg::tiles_m_bf16();
+        int64_t bound = (cdiv64(m, ts.bm) + g + 1) * cdiv64(n, ts.bn);
+        if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
+        const bool vec = aligned(lhs, 16) && aligned(rhs, 16) && k % 8 == 0 && n % 8 == 0;
+        e = gg::launch_ragged_m_bf16(p, persistent_grid(bound, 1, cus), vec, s);
+    } else {
+        gg::TileShape ts = gg::tiles_m_e4m3();
+        int64_t bound = (cdiv64(m, ts.bm) + g + 1) * cdiv64(n, ts.bn);
+        if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
+        e = gg::launch_ragged_m_e4m3(p, persistent_grid(bound, 1, cus), s);
+    }
+    return e == hipSuccess ? GG_OK : GG_ERR_HIP;
+}
+
+gg_status run_k(const void* lhs, const void* dout, const int32_t* gs, void* out, int64_t m, int64_t k, int64_t n,
+                int32_t g, gg_dtype in, gg_dtype outd, uint32_t* status, int uniform_rows, hipStream_t s) {
+    int cus;
+    if (device_cus(&cus) != 0) return GG_ERR_HIP;
+    gg::KParams p{};
+    p.lhs = lhs; p.dout = dout; p.group_sizes = gs; p.out = out; p.status = status;
+    p.m = (int)m; p.k = (int)k; p.n = (int)n; p.g = g; p.uniform_rows = uniform_rows;
+    p.out_f32 = outd == GG_DT_F32;
+    hipError_t e;
+    if (in == GG_DT_F32) {
+        gg::TileShape ts = gg::tiles_k_f32();
+        int64_t bound = (int64_t)g * cdiv64(k, ts.bm) * cdiv64(n, ts.bn);
+        if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
+        e = gg::launch_ragged_k_f32(p, persistent_grid(bound, 4, cus), s);
+    } else {
+        gg::TileShape ts = gg::tiles_k_bf16();
+        int64_t bound = (int64_t)g * cdiv64(k, ts.bm) * cdiv64(n, ts.bn);
+        if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
+        const bool vec = aligned(lhs, 16) && aligned(dout, 16) && k % 8 == 0 && n % 8 == 0;
+        e = gg::launch_ragged_k_bf16(p, persistent_grid(bound, 1, cus), vec, s);
+    }
+    return e == hipSuccess ? GG_OK : GG_ERR_HIP;
+}
+
+bool m_dtypes_ok(gg_dtype in, gg_dtype out) {
+    if (in == GG_DT_F32) return out == GG_DT_F32;
+    if (in == GG_DT_BF16 || in == GG_DT_E4M3) return out == GG_DT_BF16 || out == GG_DT_F32;
+    return false;
+}
+bool k_dtypes_ok(gg_dtype in, gg_dtype out) {
+    if (in == GG_DT_F32) return out == GG_DT_F32;
+    if (in == GG_DT_BF16) return out == GG_DT_F32 || out == GG_DT_BF16;
+    return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gg_abi_version(void) { return GG_ABI_VERSION; }
+
+const char* gg_status_string(gg_status s) {
+    switch (s) {
+        case GG_OK: return "ok";
+        case GG_ERR_NULL_PTR: return "a required pointer is NULL";
+        case GG_ERR_BAD_SHAPE: return "bad shape (negative size, g outside [1, GG_MAX_GROUPS], or too large)";
+        case GG_ERR_BAD_DTYPE: return "unsupported element type combination";
+        case GG_ERR_MISALIGNED: return "misaligned pointer";
+        case GG_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case GG_ERR_UNSUPPORTED: return "unsupported argument combination";
+        case GG_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t gg_workspace_bytes(gg_op op, int64_t m, int64_t k, int64_t n, int32_t g, int64_t capacity, gg_dtype in) {
+    if (m < 0 || k < 0 || n < 0 || g < 1 || g > GG_MAX_GROUPS) return 0;
+    if (in != GG_DT_F32 && in != GG_DT_BF16 && in != GG_DT_E4M3) return 0;
+    switch (op) {
+        case GG_OP_RAGGED_M:
+        case GG_OP_RAGGED_K: return kHeader;
+        case GG_OP_PADDED_M: {
+            if (capacity < 1) return 0;
+            const size_t rows = (size_t)g * (size_t)capacity;
+            size_t b = kHeader;
+            b += align_up(rows * (size_t)k * elem_bytes(in), 256);    // padded lhs
+            b += align_up(rows * (size_t)n * 4, 256);                 // padded result (room for fp32)
+            if (in == GG_DT_E4M3) b += align_up(rows * (size_t)(k / 32), 256);   // padded lhs scales
+            return b;
+        }
+        case GG_OP_PADDED_K: {
+            if (capacity < 1) return 0;
+            const size_t rows = (size_t)g * (size_t)capacity;
+            return kHeader + align_up(rows * (size_t)k * elem_bytes(in), 256) + align_up(rows * (size_t)n * elem_bytes(in), 256);
+        }
+    }
+    return 0;
+}
+
+gg_status ragged_dot_m(const void* lhs, const void* rhs, const int32_t* group_sizes, void* out, int64_t m, int64_t k,
+                       int64_t n, int32_t g, gg_dtype in_dtype, gg_dtype out_dtype, const uint8_t* lhs_scale,
+                       const uint8_t* rhs_scale, void* workspace, size_t workspace_bytes, void* stream) {
+    gg_status st = check_common(m, k, n, g, group_sizes, workspace, workspace_bytes, kHeader);
+    if (st != GG_OK) return st;
+    if (!m_dtypes_ok(in_dtype, out_dtype)) return GG_ERR_BAD_DTYPE;
+    if ((m * k > 0 && !lhs) || (k * n > 0 && !rhs) || (m * n > 0 && !out)) return GG_ERR_NULL_PTR;
+    const size_t es = elem_bytes(in_dtype);
+    if (!aligned(lhs, es) || !aligned(rhs, es) || !aligned(out, elem_bytes(out_dtype))) return GG_ERR_MISALIGNED;
+    if (in_dtype == GG_DT_E4M3) {
+        if (k % 32 != 0) return GG_ERR_UNSUPPORTED;
+        if ((m * k > 0 && !lhs_scale) || (k * n > 0 && !rhs_scale)) return GG_ERR_NULL_PTR;
+        if (!aligned(lhs, 16) || !aligned(rhs, 16)) return GG_ERR_MISALIGNED;
+    }
+    return run_m(lhs, rhs, group_sizes, out, m, k, n, g, in_dtype, out_dtype, lhs_scale, rhs_scale, (uint32_t*)workspace,
+                 0, (hipStream_t)stream);
+}
+
+gg_status ragged_dot_k(const void* lhs, const void* dout, const int32_t* group_sizes, void* out, int64_t m, int64_t k,
+                       int64_t n, int32_t g, gg_dtype in_dtype, gg_dtype out_dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    gg_status st = check_common(m, k, n, g, group_sizes, workspace, workspace_bytes, kHeader);
+    if (st != GG_OK) return st;
+    if (!k_dtypes_ok(in_dtype, out_dtype)) return GG_ERR_BAD_DTYPE;
+    if ((m * k > 0 && !lhs) || (m * n > 0 && !dout) || (k * n > 0 && !out)) return GG_ERR_NULL_PTR;
+    const size_t es = elem_bytes(in_dtype);
+    if (!aligned(lhs, es) || !aligned(dout, es) || !aligned(out, elem_bytes(out_dtype))) return GG_ERR_MISALIGNED;
+    return run_k(lhs, dout, group_sizes, out, m, k, n, g, in_dtype, out_dtype, (uint32_t*)workspace, 0,
+                 (hipStream_t)stream);
+}
+
+gg_status padded_dot(gg_op mode, const void* a, const void* b, const int32_t* group_sizes, void* out, int64_t m,
+                     int64_t k, int64_t n, int32_t g, int64_t capacity, gg_dtype in_dtype, gg_dtype out_dtype,
+                     const uint8_t* a_scale, const uint8_t* b_scale, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    if (mode != GG_OP_PADDED_M && mode != GG_OP_PADDED_K) return GG_ERR_UNSUPPORTED;
+    if (capacity < 1 || !fits_i32(capacity) || !fits_i32((int64_t)g * capacity)) return GG_ERR_BAD_SHAPE;
+    const size_t need = gg_workspace_bytes(mode, m, k, n, g, capacity, in_dtype);
+    gg_status st = check_common(m, k, n, g, group_sizes, workspace, workspace_bytes, need ? need : kHeader);
+    if (st != GG_OK) return st;
+    const bool is_m = mode == GG_OP_PADDED_M;
+    if (is_m ? !m_dtypes_ok(in_dtype, out_dtype) : !k_dtypes_ok(in_dtype, out_dtype)) return GG_ERR_BAD_DTYPE;
+    if (need == 0) return GG_ERR_BAD_SHAPE;
+    const size_t es = elem_bytes(in_dtype), os = elem_bytes(out_dtype);
+    if (!a || !b || !out) return GG_ERR_NULL_PTR;
+    if (!aligned(a, es) || !aligned(b, es) || !aligned(out, os)) return GG_ERR_MISALIGNED;
+    if (in_dtype == GG_DT_E4M3) {
+        if (!is_m) return GG_ERR_BAD_DTYPE;
+        if (k % 32 != 0) return GG_ERR_UNSUPPORTED;
+        if (!a_scale || !b_scale) return GG_ERR_NULL_PTR;
+        if (!aligned(a, 16) || !aligned(b, 16)) return GG_ERR_MISALIGNED;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    uint32_t* status = (uint32_t*)workspace;
+    uint8_t* base = (uint8_t*)workspace + kHeader;
+    const int64_t rows = (int64_t)g * capacity;
+    uint8_t* pa = base;
+    uint8_t* pb = pa + align_up((size_t)rows * (size_t)k * es, 256);
+    hipError_t e;
+    if (is_m) {
+        // 1. expand: lhs rows -> [g, C, k] (+ their scales)
+        e = gg::launch_pad_scatter(a, pa, group_sizes, (int)m, g, (int)capacity, (long long)k * (long long)es, status, s);
+        if (e != hipSuccess) return GG_ERR_HIP;
+        uint8_t* psc = pb + align_up((size_t)rows * (size_t)n * 4, 256);
+        if (in_dtype == GG_DT_E4M3) {
+            e = gg::launch_pad_scatter(a_scale, psc, group_sizes, (int)m, g, (int)capacity, (long long)(k / 32), nullptr, s);
+            if (e != hipSuccess) return GG_ERR_HIP;
+        }
+        // 2. one uniform batched GEMM [g, C, k] x [g, k, n] -> [g, C, n]
+        st = run_m(pa, b, group_sizes, pb, rows, k, n, g, in_dtype, out_dtype, psc, b_scale, nullptr, (int)capacity, s);
+        if (st != GG_OK) return st;
+        // 3. compact: [g, C, n] -> [m, n]
+        e = gg::launch_pad_gather(pb, out, group_sizes, (int)m, g, (int)capacity, (long long)n * (long long)os, s);
+        return e == hipSuccess ? GG_OK : GG_ERR_HIP;
+    }
+    // contracting form: expand both operands, then one uniform batched contraction
+    e = gg::launch_pad_scatter(a, pa, group_sizes, (int)m, g, (int)capacity, (long long)k * (long long)es, status, s);
+    if (e != hipSuccess) return GG_ERR_HIP;
+    e = gg::launch_pad_scatter(b, pb, group_sizes, (int)m, g, (int)capacity, (long long)n * (long long)es, nullptr, s);
+    if (e != hipSuccess) return GG_ERR_HIP;
+    return run_k(pa, pb, group_sizes, out, rows, k, n, g, in_dtype, out_dtype, nullptr, (int)capacity, s);
+}
+
+gg_status gg_schedule(const int32_t* group_sizes, int64_t m, int64_t n, int32_t g, int32_t block_m, int32_t block_n,
+                      int32_t* row_off, int32_t* tile_off, uint32_t* status, void* stream) {
+    if (!group_sizes || !row_off || !tile_off || !status) return GG_ERR_NULL_PTR;
+    if (m < 0 || n < 0 || g < 1 || g > GG_MAX_GROUPS || !fits_i32(m) || !fits_i32(n)) return GG_ERR_BAD_SHAPE;
+    if (block_m < 1 || block_m > 4096 || block_n < 1 || block_n > 4096) return GG_ERR_BAD_SHAPE;
+    if (!aligned(group_sizes, 4) || !aligned(row_off, 4) || !aligned(tile_off, 4) || !aligned(status, 4))
+        return GG_ERR_MISALIGNED;
+    hipError_t e = gg::launch_schedule(group_sizes, (int)m, (int)n, g, block_m, block_n, row_off, tile_off, status,
+                                       (hipStream_t)stream);
+    return e == hipSuccess ? GG_OK : GG_ERR_HIP;
+}
+
+gg_status gg_read_device_status(const void* workspace, uint32_t* flags, void* stream) {
+    if (!workspace || !flags) return GG_ERR_NULL_PTR;
+    hipStream_t s = (hipStream_t)stream;
+    if (hipStreamSynchronize(s) != hipSuccess) return GG_ERR_HIP;
+    if (hipMemcpy(flags, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess) return GG_ERR_HIP;
+    return GG_OK;
+}
+
+}  // extern "C"

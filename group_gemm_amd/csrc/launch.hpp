@@ -1,0 +1,63 @@
+// launch.hpp -- parameter blocks and host-side launchers of the gfx950 kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "groupgemm.h"
+
+namespace gg {
+
+// Non-contracting ragged dot: out[m,n] = per-group lhs[m,k] . rhs[g,k,n].
+struct MParams {
+    const void* lhs;            // [m,k]
+    const void* rhs;            // [g,k,n]
+    const uint8_t* lhs_scale;   // [m,k/32]   (e4m3 only)
+    const uint8_t* rhs_scale;   // [g,k/32,n] (e4m3 only)
+    const int32_t* group_sizes; // [g] device, or NULL when uniform_rows > 0
+    void* out;                  // [m,n]
+    uint32_t* status;           // device status word, written by workgroup 0
+    int m, k, n, g;
+    int uniform_rows;           // > 0: every group has exactly this many rows (batched form)
+    int out_f32;                // 1: fp32 output, 0: bf16 output
+};
+
+// Contracting ragged dot: out[g,k,n] = per-group lhs[rows,k]^T . dout[rows,n].
+struct KParams {
+    const void* lhs;            // [m,k]
+    const void* dout;           // [m,n]
+    const int32_t* group_sizes;
+    void* out;                  // [g,k,n]
+    uint32_t* status;
+    int m, k, n, g;
+    int uniform_rows;
+    int out_f32;
+};
+
+// Kernel families.  Each launcher returns the hipError_t of its launch.
+hipError_t launch_ragged_m_bf16(const MParams& p, int grid, bool vec, hipStream_t s);
+hipError_t launch_ragged_m_f32(const MParams& p, int grid, hipStream_t s);
+hipError_t launch_ragged_m_e4m3(const MParams& p, int grid, hipStream_t s);
+hipError_t launch_ragged_k_bf16(const KParams& p, int grid, bool vec, hipStream_t s);
+hipError_t launch_ragged_k_f32(const KParams& p, int grid, hipStream_t s);
+
+// Static tile geometry of each family (host-side grid sizing).
+struct TileShape { int bm, bn; };
+TileShape tiles_m_bf16();
+TileShape tiles_m_f32();
+TileShape tiles_m_e4m3();
+TileShape tiles_k_bf16();   // bm along k (output rows), bn along n
+TileShape tiles_k_f32();
+
+// padded_dot helpers: scatter rows of `src` [m, row_elems] into `dst` [g, cap, row_elems]
+// (zero-filling the padding), and gather rows back.  elem_bytes in {1, 2, 4}.
+hipError_t launch_pad_scatter(const void* src, void* dst, const int32_t* group_sizes, int m, int g,
+                              int cap, long long row_bytes, uint32_t* status, hipStream_t s);
+hipError_t launch_pad_gather(const void* src, void* dst, const int32_t* group_sizes, int m, int g,
+                             int cap, long long row_bytes, hipStream_t s);
+
+// Scan-only kernel behind gg_schedule.
+hipError_t launch_schedule(const int32_t* group_sizes, int m, int n, int g, int bm, int bn,
+                           int32_t* row_off, int32_t* tile_off, uint32_t* status, hipStream_t s);
+
+}  // namespace gg

@@ -1,0 +1,155 @@
+/*
+ * groupgemm.h -- C ABI of the MI355X (gfx950) ragged-dot Group-GEMM library.
+ *
+ * The operation is ragged-dot lowered to one Group-GEMM: a set of independent GEMMs whose
+ * row counts are known only at run time, computed in one launch with no padding.
+ * Sources (page titles and sections):
+ *   "Group-GEMM in XLA: Making Mixture-of-Experts Fast and Memory-Efficient" (AMD ROCm blog):
+ *     Part 1 "The Ragged-Dot Operation" (lhs [m,k], rhs [g,k,n], group_sizes [g], 2-D out),
+ *     "Why Group-GEMM Is the Suitable Solution", "The Naive Support, and Why It Hurts:
+ *     Padded-Dot"; Part 3 "Non-Contracting (the MoE Case)", "Contracting", "Batch";
+ *     Part 4 Table 7 (fwd / dgrad / wgrad classes).
+ *   "[Triton/Gluon] Merge MoE MXFP8 GEMM into existing _moe_gemm_a8w8 kernel" (ROCm/aiter
+ *     pull request 5658): OCP e4m3 with one E8M0 scale per 32 elements along k, a
+ *     zero-filled output, and a routing conversion with no host synchronisation.
+ *
+ * Conventions shared by every call
+ *   - All tensors are caller-owned device memory, dense row-major (last index fastest).
+ *     `out` must not overlap any input.  The library allocates and frees nothing.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *     returns once it is enqueued.  No call synchronises with the host, reads group_sizes
+ *     on the host, or allocates, so every call may be captured in a HIP graph.
+ *   - group_sizes is int32[g] in device memory.  Group h owns the contiguous rows
+ *     [sum_{j<h} gs_j, sum_{j<=h} gs_j).  Bad sizes are a device-side condition: a negative
+ *     size counts as 0 and the groups are cut off at row m (no access out of bounds); the
+ *     device status word of the workspace records it (GG_DEV_*).
+ *   - Host-detectable errors return a code and enqueue nothing.
+ *   - Accumulation is fp32.  bf16 outputs are rounded to nearest-even.
+ *   - Tensors must be aligned to their element size (e4m3 operands: 16 bytes) and the
+ *     workspace to 16 bytes.  16-byte aligned bf16 operands whose rows are whole multiples
+ *     of 16 bytes take the vectorised path (the one performance figures assume); any other
+ *     k and n take an element-wise path.
+ */
+#ifndef GROUPGEMM_H
+#define GROUPGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GG_ABI_VERSION 1
+
+typedef enum {
+    GG_OK = 0,
+    GG_ERR_NULL_PTR = 1,           /* a required pointer is NULL                          */
+    GG_ERR_BAD_SHAPE = 2,          /* negative m/k/n, g < 1, g above GG_MAX_GROUPS, ...    */
+    GG_ERR_BAD_DTYPE = 3,          /* unsupported in/out element type combination          */
+    GG_ERR_MISALIGNED = 4,         /* a pointer is not 4-byte aligned                       */
+    GG_ERR_WORKSPACE_TOO_SMALL = 5,
+    GG_ERR_UNSUPPORTED = 6,        /* e.g. MXFP8 with k not a multiple of 32               */
+    GG_ERR_HIP = 7                 /* a HIP runtime call failed (launch, device query)      */
+} gg_status;
+
+typedef enum {
+    GG_DT_F32 = 0,                 /* IEEE binary32                                         */
+    GG_DT_BF16 = 1,                /* bfloat16                                              */
+    GG_DT_E4M3 = 2                 /* OCP float8 e4m3 ("e4m3fn"), with E8M0 block scales    */
+} gg_dtype;
+
+typedef enum {
+    GG_OP_RAGGED_M = 0,            /* ragged_dot_m                                          */
+    GG_OP_RAGGED_K = 1,            /* ragged_dot_k                                          */
+    GG_OP_PADDED_M = 2,            /* padded_dot, non-contracting form                      */
+    GG_OP_PADDED_K = 3             /* padded_dot, contracting form                          */
+} gg_op;
+
+/* Device status bits (read back with gg_read_device_status). */
+#define GG_DEV_NEGATIVE_SIZE 0x1u  /* some group_sizes[h] < 0 (treated as 0)               */
+#define GG_DEV_SUM_EXCEEDS_M 0x2u  /* sum(group_sizes) > m (groups cut off at row m)       */
+#define GG_DEV_OVER_CAPACITY 0x4u  /* padded_dot: a group had more rows than `capacity`    */
+
+/* Largest group count any call accepts. */
+#define GG_MAX_GROUPS 1024
+
+/* Workspace bytes a call needs.  Tiny (a few hundred bytes) for the ragged calls; for
+ * padded_dot it holds the padded operands and result ([g, capacity, .] buffers).
+ * in_dtype selects the element size of the padded buffers.  Returns 0 on bad arguments. */
+size_t gg_workspace_bytes(gg_op op, int64_t m, int64_t k, int64_t n, int32_t g, int64_t capacity,
+                          gg_dtype in_dtype);
+
+/* ragged_dot_m -- non-contracting (m-ragged) ragged dot, the MoE forward case.
+ * ("Group-GEMM in XLA", Part 1 "The Ragged-Dot Operation"; Part 3 "Non-Contracting".)
+ *   out[r, :] = lhs[r, :] . rhs[h]   for every row r of group h;   rows r >= sum(sizes) = 0.
+ *   lhs  [m, k]      in_dtype        (fp32, bf16 or e4m3)
+ *   rhs  [g, k, n]   in_dtype        one weight matrix per group, n fastest
+ *   out  [m, n]      out_dtype       fp32 for fp32 inputs; bf16 or fp32 otherwise
+ *   lhs_scale [m, k/32], rhs_scale [g, k/32, n]: E8M0 bytes, required for e4m3 inputs
+ *     (value = e4m3 * 2^(scale - 127)), NULL otherwise; e4m3 needs k % 32 == 0.
+ * The table-7 class fwd_wo is the same call with k and n renamed.  Every element of out is
+ * written on every call. */
+gg_status ragged_dot_m(const void* lhs, const void* rhs, const int32_t* group_sizes, void* out,
+                       int64_t m, int64_t k, int64_t n, int32_t g, gg_dtype in_dtype,
+                       gg_dtype out_dtype, const uint8_t* lhs_scale, const uint8_t* rhs_scale,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ragged_dot_k -- contracting ragged dot, the weight-gradient case: the contracted
+ * dimension m is ragged and the group index appears in the output.
+ * ("Group-GEMM in XLA", Part 3 "Contracting"; Part 4 Table 7, class wgrad_wi.)
+ *   out[h] = lhs[rows of h, :]^T . dout[rows of h, :]   for every group h; empty group -> 0
+ *   lhs  [m, k]      in_dtype (fp32 or bf16)
+ *   dout [m, n]      in_dtype
+ *   out  [g, k, n]   out_dtype (fp32, or bf16 for bf16 inputs); every element written.
+ * wgrad_wo is the same call with the operands' roles swapped. */
+gg_status ragged_dot_k(const void* lhs, const void* dout, const int32_t* group_sizes, void* out,
+                       int64_t m, int64_t k, int64_t n, int32_t g, gg_dtype in_dtype,
+                       gg_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* padded_dot -- the capacity-padded baseline the Group-GEMM replaces.
+ * ("Group-GEMM in XLA", Part 1 "The Naive Support, and Why It Hurts: Padded-Dot" and Part 4:
+ * expand the ragged operand into g padded matrices, one batched GEMM, compact again.)
+ *   mode GG_OP_PADDED_M: a = lhs [m,k], b = rhs [g,k,n], out [m,n]; same result as
+ *     ragged_dot_m when capacity >= max(group_sizes).
+ *   mode GG_OP_PADDED_K: a = lhs [m,k], b = dout [m,n], out [g,k,n]; same result as
+ *     ragged_dot_k when capacity >= max(group_sizes).
+ *   Rows of a group past `capacity` are dropped (they contribute nothing and their output
+ *   rows are 0) and GG_DEV_OVER_CAPACITY is set.  Steps: scatter into the zeroed
+ *   [g, capacity, .] buffers of the workspace, one uniform batched GEMM, gather.
+ *   a_scale / b_scale: as lhs_scale / rhs_scale of ragged_dot_m (mode M with e4m3 only). */
+gg_status padded_dot(gg_op mode, const void* a, const void* b, const int32_t* group_sizes,
+                     void* out, int64_t m, int64_t k, int64_t n, int32_t g, int64_t capacity,
+                     gg_dtype in_dtype, gg_dtype out_dtype, const uint8_t* a_scale,
+                     const uint8_t* b_scale, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* gg_schedule -- runs only the group_sizes -> offsets scan that opens every launch, and
+ * writes its tables, so the scan can be tested on its own.
+ * ("Group-GEMM in XLA", Part 2 "The Compile-Time vs. Runtime Problem": a block scan over
+ * the group sizes gives every group its start; Part 3 "Non-Contracting": exclusive
+ * prefix = start rows, inclusive = end rows.)
+ *   row_off  int32[g+1]  device: clamped exclusive prefix of the sizes; row_off[g] = rows used
+ *   tile_off int32[g+1]  device: exclusive prefix of per-group tile counts
+ *                        ceil(size_h / block_m) * ceil(n / block_n)
+ *   status   uint32[1]   device: GG_DEV_* bits
+ *   block_m, block_n in [1, 4096]. */
+gg_status gg_schedule(const int32_t* group_sizes, int64_t m, int64_t n, int32_t g, int32_t block_m,
+                      int32_t block_n, int32_t* row_off, int32_t* tile_off, uint32_t* status,
+                      void* stream);
+
+/* Synchronises `stream`, then copies the device status word of `workspace` (written by the
+ * last call that used it) into *flags.  For tests and debugging. */
+gg_status gg_read_device_status(const void* workspace, uint32_t* flags, void* stream);
+
+/* Static text for a status code. */
+const char* gg_status_string(gg_status s);
+
+/* GG_ABI_VERSION of the built library. */
+int gg_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GROUPGEMM_H */

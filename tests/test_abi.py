@@ -1,0 +1,99 @@
+"""The C-ABI library loads, exports every symbol its header declares, and rejects bad
+arguments on the host before touching the GPU.  CPU only: every call below fails host
+validation, so no pointer passed here is ever dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from group_gemm_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "groupgemm.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("ragged_dot_m", "ragged_dot_k", "padded_dot", "gg_workspace_bytes", "gg_schedule",
+                     "gg_read_device_status", "gg_status_string", "gg_abi_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_strings():
+    assert B.abi_version() == 1
+    for code in range(8):
+        assert B.status_string(code)
+
+
+# fake, aligned, never-dereferenced addresses
+P = ctypes.c_void_p(0x10000)
+NULL = None
+WS_SMALL = 8
+
+
+def _m(lhs=P, rhs=P, gs=P, out=P, m=64, k=64, n=64, g=4, ind=1, outd=1, ls=NULL, rs=NULL, ws=P, wsb=4096):
+    return B.lib().ragged_dot_m(lhs, rhs, gs, out, m, k, n, g, ind, outd, ls, rs, ws, wsb, None)
+
+
+def test_ragged_m_host_validation():
+    assert _m(gs=NULL) == 1                      # GG_ERR_NULL_PTR
+    assert _m(lhs=NULL) == 1
+    assert _m(ws=NULL) == 1
+    assert _m(g=0) == 2                          # GG_ERR_BAD_SHAPE
+    assert _m(g=1025) == 2
+    assert _m(m=-1) == 2
+    assert _m(k=1 << 31) == 2
+    assert _m(ind=0, outd=1) == 3                # fp32 in -> bf16 out: GG_ERR_BAD_DTYPE
+    assert _m(ind=7) == 3
+    assert _m(ws=ctypes.c_void_p(0x10004)) == 4  # workspace not 16-byte aligned
+    assert _m(lhs=ctypes.c_void_p(0x10001)) == 4 # bf16 operand on an odd address
+    assert _m(wsb=WS_SMALL) == 5                 # GG_ERR_WORKSPACE_TOO_SMALL
+    assert _m(ind=2, k=48, ls=P, rs=P) == 6      # e4m3 needs k % 32 == 0
+    assert _m(ind=2, k=64, ls=NULL, rs=P) == 1   # e4m3 needs scales
+
+
+def test_ragged_k_host_validation():
+    L = B.lib()
+    assert L.ragged_dot_k(P, P, NULL, P, 64, 64, 64, 4, 1, 0, P, 4096, None) == 1
+    assert L.ragged_dot_k(P, P, P, P, 64, 64, 64, 0, 1, 0, P, 4096, None) == 2
+    assert L.ragged_dot_k(P, P, P, P, 64, 64, 64, 4, 2, 0, P, 4096, None) == 3   # e4m3 not offered
+    assert L.ragged_dot_k(P, P, P, P, 64, 64, 64, 4, 1, 0, P, 8, None) == 5
+
+
+def test_padded_host_validation():
+    L = B.lib()
+    assert L.padded_dot(0, P, P, P, P, 64, 64, 64, 4, 16, 1, 1, NULL, NULL, P, 1 << 30, None) == 6   # bad mode
+    assert L.padded_dot(2, P, P, P, P, 64, 64, 64, 4, 0, 1, 1, NULL, NULL, P, 1 << 30, None) == 2   # capacity 0
+    need = B.workspace_bytes("padded_m", 64, 64, 64, 4, 16)
+    assert need > 256
+    assert L.padded_dot(2, P, P, P, P, 64, 64, 64, 4, 16, 1, 1, NULL, NULL, P, need - 1, None) == 5
+    assert L.padded_dot(3, P, P, P, P, 64, 64, 64, 4, 16, 2, 0, P, P, P, 1 << 30, None) == 3        # e4m3 k-mode
+
+
+def test_workspace_sizes():
+    assert B.workspace_bytes("ragged_m", 8192, 4096, 14336, 8) == 256
+    assert B.workspace_bytes("ragged_k", 16384, 5120, 8192, 16) == 256
+    # padded lhs [g,C,k] bf16 + padded result room [g,C,n] fp32
+    g, C, k, n = 8, 1280, 4096, 14336
+    assert B.workspace_bytes("padded_m", 8192, k, n, g, C) >= g * C * (2 * k + 4 * n)
+    assert B.lib().gg_workspace_bytes(0, 1, 1, 1, 0, 0, 1) == 0
+
+
+def test_schedule_host_validation():
+    L = B.lib()
+    assert L.gg_schedule(P, 9, 1, 3, 0, 1, P, P, P, None) == 2
+    assert L.gg_schedule(NULL, 9, 1, 3, 3, 1, P, P, P, None) == 1

@@ -1,0 +1,292 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Bars: fp32 outputs -- normwise relative error ||Y - R||_F / ||R||_F <= 1e-5; bf16 outputs
+(bf16 and MXFP8 inputs) -- every element |Y - R| <= 1e-2 |R| + 1e-2, the MXFP8 oracle
+being fed the same e4m3 codes and E8M0 scales.  Rows past sum(group_sizes) and slabs of
+empty groups must be exactly 0, also when the output buffer starts out NaN.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from group_gemm_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def gg():
+    import group_gemm_amd
+    return group_gemm_amd
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def raw(t):
+    return W.to_numpy_raw(t)
+
+
+def check_fp32(y, ref, what):
+    y = y.double().cpu().numpy() if torch.is_tensor(y) else y
+    nr = np.linalg.norm(ref)
+    err = np.linalg.norm(y - ref)
+    rel = err / nr if nr > 0 else err
+    assert np.all(np.isfinite(y)), what
+    assert rel <= 1e-5, f"{what}: normwise relative error {rel:.3e}"
+
+
+def check_bf16(y, ref, what):
+    y = y.double().cpu().numpy() if torch.is_tensor(y) else y
+    bad = np.abs(y - ref) > 1e-2 * np.abs(ref) + 1e-2
+    assert np.all(np.isfinite(y)), what
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements outside the bf16 bar, max |d| {np.abs(y - ref).max():.3e}"
+
+
+def run_m(d, out_dtype=None, poison=True):
+    m, n = d["lhs"].shape[0], d["rhs"].shape[2]
+    if out_dtype is None:
+        out_dtype = torch.float32 if d["lhs"].dtype == torch.float32 else torch.bfloat16
+    out = torch.full((m, n), float("nan"), dtype=out_dtype, device=DEV) if poison else None
+    y = gg().ragged_dot_m(d["lhs"], d["rhs"], d["group_sizes"], out=out, out_dtype=out_dtype,
+                          lhs_scale=d.get("lhs_scale"), rhs_scale=d.get("rhs_scale"))
+    torch.cuda.synchronize()
+    return y
+
+
+def oracle_m(d, rows=None):
+    return oracle.ragged_dot_m(raw(d["lhs"]), raw(d["rhs"]), raw(d["group_sizes"]),
+                               raw(d["lhs_scale"]) if "lhs_scale" in d else None,
+                               raw(d["rhs_scale"]) if "rhs_scale" in d else None, rows=rows)
+
+
+def to_dev(d):
+    return {key: v.to(DEV) for key, v in d.items()}
+
+
+# ---- the scan / tile table --------------------------------------------------------------
+
+def test_schedule_table2_and_tiny():
+    say("schedule: [3,2,4] BM=3; [16,0,40,8] BM=16; invalid sizes")
+    gs = torch.tensor([3, 2, 4], dtype=torch.int32, device=DEV)
+    row_off, tile_off, status = gg().build_schedule(gs, 9, 1, 3, 1)
+    assert row_off.tolist() == [0, 3, 5, 9] and tile_off.tolist() == [0, 1, 2, 4] and status.item() == 0
+    gs = torch.tensor([16, 0, 40, 8], dtype=torch.int32, device=DEV)
+    row_off, tile_off, status = gg().build_schedule(gs, 64, 1, 16, 1)
+    assert row_off.tolist() == [0, 16, 16, 56, 64] and tile_off.tolist() == [0, 1, 1, 4, 5]
+    # n-tiles multiply the per-group tile count
+    row_off, tile_off, _ = gg().build_schedule(gs, 64, 100, 16, 32)
+    assert tile_off.tolist() == [0, 4, 4, 16, 20]
+    gs = torch.tensor([-3, 4, 9, 2], dtype=torch.int32, device=DEV)
+    row_off, tile_off, status = gg().build_schedule(gs, 10, 1, 4, 1)
+    assert row_off.tolist() == [0, 0, 4, 10, 10] and status.item() == 3
+    # many groups: compare with a plain numpy scan
+    r = np.random.default_rng(0)
+    sizes = r.integers(0, 40, 1024).astype(np.int32)
+    m = int(sizes.sum())
+    row_off, tile_off, status = gg().build_schedule(torch.from_numpy(sizes).to(DEV), m, 300, 32, 64)
+    ro = np.concatenate([[0], np.cumsum(sizes)])
+    to = np.concatenate([[0], np.cumsum(-(-sizes // 32) * 5)])
+    assert np.array_equal(row_off.cpu().numpy(), ro) and np.array_equal(tile_off.cpu().numpy(), to)
+
+
+# ---- ragged_dot_m -----------------------------------------------------------------------
+
+def test_tiny_fp32_workload():
+    w = W.WORKLOADS["tiny_fp32"]
+    say(w.name)
+    d = W.make_inputs(w, device=DEV)
+    y = run_m(d)
+    ref = oracle_m(d)
+    check_fp32(y, ref, w.name)
+    assert torch.all(y[64:] == 0)
+
+
+M_CASES = [
+    # (m, k, n, group_sizes)
+    (300, 256, 512, [100, 0, 150, 50]),          # several tiles, an empty group
+    (300, 256, 512, [0, 300, 0, 0]),             # one full group
+    (300, 192, 264, [7, 1, 255, 256, 0]),        # sum < m: tail zeros; ragged n tail
+    (513, 96, 136, [257, 256]),                  # k not a multiple of 64, m-tile +1 rows
+    (64, 32, 64, [64]),                          # g = 1
+    (40, 8, 16, [3, 0, 37]),                     # k = 8
+    (100, 72, 100, [30, 30, 40]),                # n % 8 != 0 -> element-wise path
+    (90, 50, 24, [45, 45]),                      # k % 8 != 0 -> element-wise path
+    (2048, 64, 64, [2] * 1024),                  # g = 1024
+    (700, 128, 256, [1, 255, 256, 257, 0, 1]),   # sizes around the 256-row tile
+]
+
+
+@pytest.mark.parametrize("case", range(len(M_CASES)))
+def test_ragged_m_bf16_small(case):
+    m, k, n, gs = M_CASES[case]
+    say("ragged_m bf16", m, k, n, len(gs))
+    d = to_dev(W.small_inputs("m", "bf16", m, k, n, gs, seed=case))
+    y = run_m(d)
+    ref = oracle_m(d)
+    check_bf16(y, ref, f"m-case {case}")
+    S = sum(gs)
+    assert torch.all(y[S:] == 0)
+    y32 = run_m(d, out_dtype=torch.float32)
+    check_fp32(y32, ref, f"m-case {case} fp32 out")
+
+
+@pytest.mark.parametrize("case", [0, 2, 3, 6])
+def test_ragged_m_fp32_small(case):
+    m, k, n, gs = M_CASES[case]
+    say("ragged_m fp32", m, k, n, len(gs))
+    d = to_dev(W.small_inputs("m", "f32", m, k, n, gs, seed=case))
+    y = run_m(d)
+    check_fp32(y, oracle_m(d), f"fp32 m-case {case}")
+    assert torch.all(y[sum(gs):] == 0)
+
+
+MX_CASES = [
+    (300, 256, 512, [100, 0, 150, 50]),
+    (513, 96, 136, [257, 256]),
+    (64, 32, 64, [64]),
+    (700, 128, 264, [1, 255, 256, 150, 0, 1]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(MX_CASES)))
+def test_ragged_m_mxfp8_small(case):
+    m, k, n, gs = MX_CASES[case]
+    say("ragged_m mxfp8", m, k, n, len(gs))
+    d = to_dev(W.small_inputs("m", "mxfp8", m, k, n, gs, seed=case))
+    y = run_m(d)
+    ref = oracle_m(d)
+    check_bf16(y, ref, f"mx case {case}")
+    assert torch.all(y[sum(gs):] == 0)
+
+
+def test_device_status_and_clamping():
+    say("invalid group sizes")
+    m, k, n = 200, 64, 64
+    gs = [-5, 120, 150, 3]       # effective 0, 120, 80 (cut at m), 0
+    d = to_dev(W.small_inputs("m", "bf16", m, k, n, [0, 120, 80, 0], seed=3))
+    d["group_sizes"] = torch.tensor(gs, dtype=torch.int32, device=DEV)
+    ws = torch.zeros(256, dtype=torch.uint8, device=DEV)
+    y = gg().ragged_dot_m(d["lhs"], d["rhs"], d["group_sizes"], workspace=ws)
+    assert gg().read_device_status(ws) == 3
+    check_bf16(y, oracle_m(d), "clamped sizes")
+    d["group_sizes"] = torch.tensor([0, 120, 80, 0], dtype=torch.int32, device=DEV)
+    gg().ragged_dot_m(d["lhs"], d["rhs"], d["group_sizes"], workspace=ws)
+    assert gg().read_device_status(ws) == 0
+
+
+# ---- ragged_dot_k -----------------------------------------------------------------------
+
+K_CASES = [
+    (300, 256, 512, [100, 0, 150, 50]),
+    (513, 96, 136, [257, 256]),
+    (64, 32, 64, [64]),
+    (700, 264, 128, [1, 255, 256, 150, 0, 1]),   # sum < m: trailing rows ignored
+    (100, 72, 100, [30, 30, 40]),                 # unaligned -> element-wise path
+    (64, 256, 256, [0, 0, 0, 0]),                 # all groups empty
+]
+
+
+@pytest.mark.parametrize("case", range(len(K_CASES)))
+@pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
+def test_ragged_k_small(case, in_dtype):
+    m, k, n, gs = K_CASES[case]
+    say("ragged_k", in_dtype, m, k, n, len(gs))
+    d = to_dev(W.small_inputs("k", in_dtype, m, k, n, gs, seed=case))
+    out = torch.full((len(gs), k, n), float("nan"), dtype=torch.float32, device=DEV)
+    y = gg().ragged_dot_k(d["lhs"], d["dout"], d["group_sizes"], out=out)
+    torch.cuda.synchronize()
+    ref = oracle.ragged_dot_k(raw(d["lhs"]), raw(d["dout"]), raw(d["group_sizes"]))
+    for h, s in enumerate(gs):
+        if s == 0:
+            assert torch.all(y[h] == 0), f"empty group {h}"
+    if np.any(ref != 0):
+        check_fp32(y, ref, f"k-case {case}")
+    if in_dtype == "bf16":
+        yb = gg().ragged_dot_k(d["lhs"], d["dout"], d["group_sizes"], out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        check_bf16(yb, ref, f"k-case {case} bf16 out")
+
+
+# ---- padded_dot -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f32", "mxfp8"])
+def test_padded_m_matches_oracle(in_dtype):
+    m, k, n, gs = 300, 128, 264, [100, 0, 150, 50]
+    say("padded_m", in_dtype)
+    d = to_dev(W.small_inputs("m", in_dtype, m, k, n, gs, seed=7))
+    ref = oracle_m(d)
+    for cap in (max(gs), 256, m):
+        y = gg().padded_dot("m", d["lhs"], d["rhs"], d["group_sizes"], cap, a_scale=d.get("lhs_scale"),
+                            b_scale=d.get("rhs_scale"))
+        torch.cuda.synchronize()
+        (check_fp32 if in_dtype == "f32" else check_bf16)(y, ref, f"padded m cap {cap}")
+
+
+def test_padded_m_over_capacity_drops_rows():
+    say("padded_m over capacity")
+    m, k, n, gs = 120, 64, 64, [50, 70]
+    d = to_dev(W.small_inputs("m", "bf16", m, k, n, gs, seed=8))
+    ws = torch.empty(gg().workspace_bytes("padded_m", m, k, n, 2, 60), dtype=torch.uint8, device=DEV)
+    y = gg().padded_dot("m", d["lhs"], d["rhs"], d["group_sizes"], 60, workspace=ws)
+    assert gg().read_device_status(ws) == 4
+    ref = oracle.padded_dot_m(raw(d["lhs"]), raw(d["rhs"]), gs, 60)
+    check_bf16(y, ref, "over capacity")
+    assert torch.all(y[110:] == 0)
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
+def test_padded_k_matches_oracle(in_dtype):
+    m, k, n, gs = 300, 128, 264, [100, 0, 150, 50]
+    say("padded_k", in_dtype)
+    d = to_dev(W.small_inputs("k", in_dtype, m, k, n, gs, seed=9))
+    ref = oracle.ragged_dot_k(raw(d["lhs"]), raw(d["dout"]), raw(d["group_sizes"]))
+    for cap in (max(gs), 300):
+        y = gg().padded_dot("k", d["lhs"], d["dout"], d["group_sizes"], cap)
+        torch.cuda.synchronize()
+        check_fp32(y, ref, f"padded k cap {cap}")
+
+
+# ---- execution model ----------------------------------------------------------------------
+
+def test_deterministic_and_stream_ordered():
+    say("determinism on a side stream")
+    m, k, n, gs = 700, 256, 512, [1, 255, 256, 150, 0, 38]
+    d = to_dev(W.small_inputs("m", "bf16", m, k, n, gs, seed=11))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a = gg().ragged_dot_m(d["lhs"], d["rhs"], d["group_sizes"])
+        b = gg().ragged_dot_m(d["lhs"], d["rhs"], d["group_sizes"])
+    s.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_graph_capture_replay():
+    say("graph capture")
+    m, k, n, gs = 700, 256, 512, [1, 255, 256, 150, 0, 38]
+    d = to_dev(W.small_inputs("m", "bf16", m, k, n, gs, seed=12))
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    eager = gg().ragged_dot_m(d["lhs"], d["rhs"], d["group_sizes"]).clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            gg().ragged_dot_m(d["lhs"], d["rhs"], d["group_sizes"], out=out, workspace=ws)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+    # new group sizes, same buffers: the graph reads them on device at replay
+    d["group_sizes"].copy_(torch.tensor([300, 0, 0, 100, 0, 0], dtype=torch.int32))
+    eager2 = gg().ragged_dot_m(d["lhs"], d["rhs"], d["group_sizes"]).clone()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), eager2.view(torch.int16))
+    assert torch.all(out[400:].float() == 0)
