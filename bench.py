@@ -1,0 +1,209 @@
+"""Benchmark of the ragged-dot Group-GEMM on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one ragged-dot call over one batch of synthetic routed-token input already
+resident in HBM (the whole hot path: group_sizes scan, tile schedule, MFMA main loop,
+masked tails, epilogue -- one kernel launch).  The default workload is the Mixtral-8x7B-
+like FFN up-projection: 4096 tokens, top-2 of 8 experts (m = 8192 rows), k = 4096,
+n = 14336, bf16 in / fp32 accumulate / bf16 out.  The timing protocol follows the pages'
+micro-benchmark (10 warm-up runs, then timed runs).
+
+Prints one JSON line: useful TFLOP/s (2 * sum(group_sizes) * k * n per step), the
+roofline of the kernel (from HIP events on the launch stream), the speedup over the
+capacity-padded baseline on the same inputs, and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+# MI355X published peaks (dense, no sparsity)
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+METRIC = "ragged-dot useful TFLOP/s + % MFMA/HBM roofline; speedup vs padded dot"
+DEFAULT_WORKLOAD = "mixtral8x7b_up_bf16"
+PROFILE_TRAFFIC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-padded", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, gs):
+    """Inputs read once (weights only of non-empty groups) plus the output written once."""
+    esz = {"bf16": 2, "f32": 4, "mxfp8": 1}[w.in_dtype]
+    osz = 4 if w.out_dtype == "f32" else 2
+    S = int(np.sum(gs))
+    nonempty = int(np.sum(np.asarray(gs) > 0))
+    if w.op == "m":
+        b = w.m * w.k * esz + nonempty * w.k * w.n * esz + w.m * w.n * osz
+        if w.in_dtype == "mxfp8":
+            b += w.m * (w.k // 32) + nonempty * (w.k // 32) * w.n
+        return b
+    return S * w.k * esz + S * w.n * esz + w.g * w.k * w.n * osz
+
+
+def useful_flops(w, gs):
+    return 2.0 * float(np.sum(gs)) * w.k * w.n
+
+
+def time_calls(fn, steps, warmup, torch):
+    """Wall time of `steps` calls (after `warmup`), synchronised on both sides, and the
+    per-launch time from HIP events recorded on the launch stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        fn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, ev0.elapsed_time(ev1) / 1e3 / steps
+
+
+def cpu_baseline(w, d, gs, target_s, W, torch):
+    """The oracle as it stands, on host cores, over a bounded sample of the workload's
+    output rows (m-ragged) or (group, k-index) rows (k-ragged); rate in TFLOP/s."""
+    import oracle
+    raw = W.to_numpy_raw
+    lhs = raw(d["lhs"])
+    gsn = raw(d["group_sizes"])
+    S = int(gsn.sum())
+    rng = np.random.default_rng(0)
+    if w.op == "m":
+        rhs = raw(d["rhs"])
+        ls = raw(d["lhs_scale"]) if "lhs_scale" in d else None
+        rs = raw(d["rhs_scale"]) if "rhs_scale" in d else None
+        per_unit = 2.0 * w.k * w.n
+        run = lambda cnt: oracle.ragged_dot_m(lhs, rhs, gsn, ls, rs, rows=rng.integers(0, S, cnt))
+        unit = "rows"
+    else:
+        dout = raw(d["dout"])
+        nonempty = np.nonzero(gsn)[0]
+        per_unit = 2.0 * float(np.mean(gsn[nonempty])) * w.n
+        def run(cnt):
+            pairs = np.stack([rng.choice(nonempty, cnt), rng.integers(0, w.k, cnt)], axis=1)
+            return oracle.ragged_dot_k(lhs, dout, gsn, pairs=pairs)
+        unit = "(group, k-index) output rows"
+    cnt, spent, done, flops = 8, 0.0, 0, 0.0
+    while spent < target_s:
+        t0 = time.perf_counter()
+        run(cnt)
+        dt = time.perf_counter() - t0
+        spent += dt
+        done += cnt
+        flops += cnt * per_unit
+        if dt < target_s / 4:
+            cnt *= 2
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(oracle.num_threads()), "kind": "oracle",
+            "sample": f"{done} {unit} of the {w.name} workload drawn uniformly, fp64 oracle, {spent:.1f} s"}
+
+
+def traffic_for(name):
+    """HBM bytes per launch measured with rocprofv3 counters for the current kernel build,
+    if such a measurement is on file."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f).get(name)
+        return None if rec is None else rec.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path would shard by "
+              "experts or tokens, see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import group_gemm_amd as G
+    from group_gemm_amd import workloads as W
+
+    G.lib()   # fail loudly if the HIP library is missing
+    w = W.WORKLOADS[a.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    gs = W.group_sizes(w)
+    d = W.make_inputs(w, device=dev, gs=gs)
+    torch.cuda.synchronize()
+    F = useful_flops(w, gs)
+    B = algorithmic_bytes(w, gs)
+
+    if w.op == "m":
+        out_dtype = torch.float32 if w.out_dtype == "f32" else torch.bfloat16
+        out = torch.empty((w.m, w.n), dtype=out_dtype, device=dev)
+        ws = torch.empty(G.workspace_bytes("ragged_m", w.m, w.k, w.n, w.g), dtype=torch.uint8, device=dev)
+        fn = lambda: G.ragged_dot_m(d["lhs"], d["rhs"], d["group_sizes"], out=out, lhs_scale=d.get("lhs_scale"),
+                                    rhs_scale=d.get("rhs_scale"), workspace=ws)
+    else:
+        out = torch.empty((w.g, w.k, w.n), dtype=torch.float32, device=dev)
+        ws = torch.empty(G.workspace_bytes("ragged_k", w.m, w.k, w.n, w.g), dtype=torch.uint8, device=dev)
+        fn = lambda: G.ragged_dot_k(d["lhs"], d["dout"], d["group_sizes"], out=out, workspace=ws)
+
+    wall, per_launch = time_calls(fn, a.steps, a.warmup, torch)
+    ms_per_step = wall / a.steps * 1e3
+    value = F / (wall / a.steps) / 1e12
+
+    # roofline of the (single) kernel: MFMA-bound if the arithmetic intensity exceeds the
+    # ridge point of its precision, else HBM-bound
+    peak_f = PEAK_TFLOPS[w.in_dtype]
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if F / B >= ridge:
+        roof = {"bound": "mfma", "achieved": F / per_launch / 1e12, "peak": peak_f, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": B / per_launch / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_for(w.name)
+
+    config = {"workload": w.name, "op": f"ragged_dot_{w.op}", "m": w.m, "k": w.k, "n": w.n, "g": w.g,
+              "group_sizes": {"min": int(gs.min()), "max": int(gs.max()), "sum": int(gs.sum()),
+                              "empty": int((gs == 0).sum())},
+              "useful_gflop_per_step": F / 1e9, "algorithmic_mb_per_step": B / 1e6,
+              "kernel_us_per_launch": per_launch * 1e6}
+
+    if not a.no_padded:
+        cap = int(math.ceil(gs.max() / 256.0) * 256)
+        pws = torch.empty(G.workspace_bytes(f"padded_{w.op}", w.m, w.k, w.n, w.g, cap, d["lhs"].dtype),
+                          dtype=torch.uint8, device=dev)
+        if w.op == "m":
+            pfn = lambda: G.padded_dot("m", d["lhs"], d["rhs"], d["group_sizes"], cap, out=out,
+                                       a_scale=d.get("lhs_scale"), b_scale=d.get("rhs_scale"), workspace=pws)
+        else:
+            pfn = lambda: G.padded_dot("k", d["lhs"], d["dout"], d["group_sizes"], cap, out=out, workspace=pws)
+        pwall, _ = time_calls(pfn, max(5, a.steps // 2), max(2, a.warmup // 2), torch)
+        p_ms = pwall / max(5, a.steps // 2) * 1e3
+        config["padded"] = {"capacity": cap, "ms_per_step": p_ms, "useful_tflops": F / (p_ms / 1e3) / 1e12,
+                            "speedup_ragged_vs_padded": p_ms / ms_per_step}
+        del pws
+
+    line = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+            "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": {"bf16": "bf16", "f32": "f32", "mxfp8": "e4m3"}[w.in_dtype],
+            "data": "synthetic (seeded routing and N(0,1) / N(0,1/k) operands)", "config": config, "roofline": roof}
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, d, gs, a.cpu_seconds, W, torch)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
