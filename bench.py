@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-padded", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 3 times (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     return ap.parse_args()
 
 
@@ -136,6 +139,14 @@ def main():
               "experts or tokens, see the design notes).", file=sys.stderr)
         sys.exit(2)
     import torch
+    if a.copy_probe:
+        src = torch.ones(a.copy_probe, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": a.copy_probe}), flush=True)
+        return
     import group_gemm_amd as G
     from group_gemm_amd import workloads as W
 

@@ -36,6 +36,9 @@ struct KParams {
 
 // Kernel families.  Each launcher returns the hipError_t of its launch.
 hipError_t launch_ragged_m_bf16(const MParams& p, int grid, bool vec, hipStream_t s);
+// vectorised bf16 kernel (16-byte aligned operands, k % 8 == 0, n % 8 == 0)
+bool ragged_m_bf16_fast_ok(const MParams& p);
+hipError_t launch_ragged_m_bf16_fast(const MParams& p, int grid, hipStream_t s);
 hipError_t launch_ragged_m_f32(const MParams& p, int grid, hipStream_t s);
 hipError_t launch_ragged_m_e4m3(const MParams& p, int grid, hipStream_t s);
 hipError_t launch_ragged_k_bf16(const KParams& p, int grid, bool vec, hipStream_t s);
