@@ -71,11 +71,13 @@ gg_status run_m(const void* lhs, const void* rhs, const int32_t* gs, void* out, 
         if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
         e = gg::launch_ragged_m_f32(p, persistent_grid(bound, 4, cus), s);
     } else if (in == GG_DT_BF16) {
+        const bool vec = aligned(lhs, 16) && aligned(rhs, 16) && aligned(out, 16) && k % 8 == 0 && n % 8 == 0;
+        const bool fast = vec && gg::ragged_m_bf16_fast_ok(p);
         gg::TileShape ts = gg::tiles_m_bf16();
+        if (fast) ts = {gg::ragged_m_bf16_fast_bm(p), 256};
         int64_t bound = (cdiv64(m, ts.bm) + g + 1) * cdiv64(n, ts.bn);
         if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
-        const bool vec = aligned(lhs, 16) && aligned(rhs, 16) && aligned(out, 16) && k % 8 == 0 && n % 8 == 0;
-        if (vec && gg::ragged_m_bf16_fast_ok(p)) e = gg::launch_ragged_m_bf16_fast(p, persistent_grid(bound, 1, cus), s);
+        if (fast) e = gg::launch_ragged_m_bf16_fast(p, persistent_grid(bound, 1, cus), s);
         else e = gg::launch_ragged_m_bf16(p, persistent_grid(bound, 1, cus), vec, s);
     } else {
         gg::TileShape ts = gg::tiles_m_e4m3();

@@ -38,6 +38,7 @@ struct KParams {
 hipError_t launch_ragged_m_bf16(const MParams& p, int grid, bool vec, hipStream_t s);
 // vectorised bf16 kernel (16-byte aligned operands, k % 8 == 0, n % 8 == 0)
 bool ragged_m_bf16_fast_ok(const MParams& p);
+int ragged_m_bf16_fast_bm(const MParams& p);   // tile rows the vectorised kernel picks (n tiles are 256 wide)
 hipError_t launch_ragged_m_bf16_fast(const MParams& p, int grid, hipStream_t s);
 hipError_t launch_ragged_m_f32(const MParams& p, int grid, hipStream_t s);
 hipError_t launch_ragged_m_e4m3(const MParams& p, int grid, hipStream_t s);

@@ -7,78 +7,148 @@
 // table, select that expert's weights, accumulate over k, masked store.  Tiles here are
 // group-aligned and walked by a persistent grid (see ragged_m.hip for the schedule notes).
 //
-// Kernel shape: 256 x 256 output tile, 4 waves in a 2 x 2 grid, each wave a 128 x 128
-// sub-tile of 4 x 4 v_mfma_f32_32x32x16_bf16 blocks (fp32 accumulators in AGPRs).
-// Operands stream through a 4-slot LDS ring of 32-wide k slices, filled by buffer loads
-// that write LDS directly (no staging registers); loads run three slices ahead of the
-// MFMAs, which is what hides HBM latency.  The buffer descriptors bound the group's rows
-// and the weight matrix, so rows past the group and the k / n tails arrive as zeros.
-// The MFMA takes the weight fragment as its first operand, which gives every lane 4
-// consecutive output columns; the epilogue stages the bf16 tile in LDS and writes whole
-// 16-byte row segments.
+// Tile: 256 x 256 outputs per workgroup, 4 waves in a 2 x 2 grid, each a 128 x 128
+// sub-tile of 4 x 4 v_mfma_f32_32x32x16_bf16 blocks (fp32 accumulators in AGPRs); k is
+// consumed in 32-wide slices.  The kernel is a template over tile rows, wave layout and
+// ring depth so other shapes can be timed; one shape is instantiated (see GG_TILE).
+//  * Operands stream through an LDS ring filled by buffer loads that write LDS directly
+//    (no staging registers), STAGES - 1 slices ahead of the MFMAs.  The buffer
+//    descriptors bound the group's rows and the weight matrix, so rows past the group and
+//    the k / n tails arrive as zeros without branches.
+//  * A rows (k-contiguous) feed the MFMA through ds_read_b128; B rows are n-contiguous
+//    (rhs as given, no per-call relayout) and ds_read_b64_tr_b16 turns them into
+//    k-consecutive fragments.
+//  * Each half slice is one pinned instruction sequence: every MFMA is followed by at
+//    most one ring load and one fragment read for the next half slice, in the order the
+//    next MFMAs need them, so LDS and memory traffic issue while the MFMAs run.
+//  * 32-row MFMA blocks that lie wholly past a group's last row are skipped (their A
+//    fragments are not read either): a group's last, partly filled tile, and tiles of
+//    short groups, cost only the blocks they need.  The block count is a template
+//    parameter of the main loop, so each variant is straight-line code.
+//  * The MFMA takes the weight fragment as its first operand, which gives every lane 4
+//    consecutive output columns; fp32 results are stored straight from AGPRs, bf16
+//    results pass through a wave-private fp32 strip in LDS (see the epilogue).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace gg {
-namespace mb3 {
+namespace mb {
 
-constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4, NT = 256;
-constexpr int CP = BN + 8;               // pitch (elements) of the staged output tile
-constexpr int SLICE = BM * BK;           // elements of one A (= one B) k slice: 16 KiB
+constexpr int BN = 256, BK = 32, NT = 256;
+constexpr int BSLICE = BK * BN;          // elements of one B slice: 16 KiB
 constexpr uint32_t kOOB = 0x80000000u;   // a buffer offset past every num_records
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
-
-struct Smem {
-    union {
-        struct {
-            uint16_t a[STAGES][SLICE];
-            uint16_t b[STAGES][SLICE];
-        } ring;
-        uint16_t c[BM * CP];
-    };
-    Tables tab;
-};
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
-__device__ inline void bstore(rsrc_t r, uint32_t off, i32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0); }
-// 16 bytes per lane from the buffer straight into LDS at lds + 16 * lane
-__device__ inline void load_lds16(rsrc_t r, const uint16_t* lds, uint32_t off) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+// the same descriptor as four scalar registers, for the inline-asm ring loads
+__device__ inline i32x4 make_rsrc_v(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = kRsrcWord3;
+    return r;
 }
-// barrier that waits for this wave's LDS accesses only; ring loads stay in flight
-__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// wait until at most `later` k slices (8 loads each per thread) are still in flight
+__device__ inline void bstore(rsrc_t r, uint32_t off, i32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0); }
+// two floats -> two bf16 (round to nearest even), low element in the low half
+__device__ inline uint32_t pack_bf16(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+// 16 bytes per lane from the buffer straight into LDS at lds + 16 * lane.  Issued from
+// inline asm so the compiler does not track it as an LDS write: its alias rule would make
+// every LDS read wait for all outstanding loads.  The kernel orders these loads itself
+// (explicit vmcnt waits, then a barrier) and issues no other vector-memory loads while
+// the ring is running, so the counts it waits on are exact.
+// lds_addr is a wave-uniform LDS byte address.
+__device__ inline void load_lds16(i32x4 r, uint32_t lds_addr, uint32_t off) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(off), "s"(r) : "memory", "m0");
+}
+// LDS byte address of a pointer into a __shared__ object
+__device__ inline uint32_t lds_u32(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+// barrier that waits for this wave's LDS accesses only; ring loads stay in flight.  The
+// builtin wait tells the compiler's own wait tracking that LDS reads issued before the
+// barrier are complete (it cannot see into the asm, and would otherwise make later
+// MFMAs wait on reads they do not use); the asm keeps the wait and the barrier together.
+__device__ inline void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt and expcnt at their maximum: no wait
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// wait until at most N vector-memory operations of this thread are outstanding
+template <int N>
+__device__ inline void wait_vm() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+// wait until at most `later` slices (PER operations each) are still in flight
+template <int PER, int MAXL>
 __device__ inline void wait_slices(int later) {
-    if (later >= 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if (later == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (MAXL > 0) {
+        if (later >= MAXL) { wait_vm<PER * MAXL>(); return; }
+        wait_slices<PER, MAXL - 1>(later);
+    } else {
+        wait_vm<0>();
+    }
 }
 
-// LDS layouts (element offsets); chunks are 8 bf16 = 16 bytes.
-// A slice [256 rows][32 k], 64-byte rows: chunk XOR (row >> 2) & 3, so the 16 rows one
-// 16-lane phase of a fragment read touches cover all 64 banks.
-__device__ inline int a_off(int r, int chunk) { return r * BK + ((chunk ^ ((r >> 2) & 3)) << 3); }
-// B slice [32 k][256 n], 512-byte rows: chunk XOR'ed in 64-byte units by a 3-bit function
-// of the row, so the rows one transpose read touches land in distinct 64-byte bank groups.
+// B slice [32 k][256 n], 512-byte rows: 16-byte chunks XOR'ed in 64-byte units by a 3-bit
+// function of the row, so the rows one transpose read touches land in distinct bank groups.
 __device__ inline int b_swz(int kr) { return ((kr & 3) | (((kr >> 3) & 1) << 2)) << 2; }
 __device__ inline int b_off(int kr, int nn) { return kr * BN + (((nn >> 3) ^ b_swz(kr)) << 3) + (nn & 7); }
+// A slice [BM rows][32 k], 64-byte rows: 16-byte chunk XOR (row >> 1) & 3.  Measured on
+// gfx950 with the fragment reads below (32 consecutive rows, one chunk per lane half), this
+// swizzle runs ds_read_b128 at ~115 B/clk per CU against ~76 for an XOR by (row >> 2) & 3.
+__device__ inline int a_off(int r, int chunk) { return r * BK + ((chunk ^ ((r >> 1) & 3)) << 3); }
 
-struct Frags { bf16x8 a[4]; bf16x8 b[4]; };
+template <int BM, int WAVES_M, int STAGES>
+struct Cfg {
+    static constexpr int BM_ROWS = BM;
+    static constexpr int WAVES_N = 4 / WAVES_M;
+    static constexpr int WROWS = BM / WAVES_M, WCOLS = BN / WAVES_N;
+    static constexpr int MI = WROWS / 32, NJ = WCOLS / 32;       // MFMA blocks per wave
+    static constexpr int ASLICE = BM * BK;
+    static constexpr int A_LOADS = BM / 64;                       // 1 KiB A blocks per wave
+    static constexpr int PER = A_LOADS + 4;                       // ring loads per thread per slice
+    static_assert(BM % 64 == 0 && WROWS % 32 == 0 && WCOLS % 32 == 0, "tile shape");
+    static_assert(PER * (STAGES - 1) <= 63, "vmcnt range");
+};
 
-// fragments of 16-wide k step s (0 or 1) of a slice
-__device__ inline void read_frags(Frags& f, const uint16_t* a, const uint16_t* b, int s, int wm, int wn) {
+template <int BM, int WAVES_M, int STAGES>
+struct Smem {
+    typedef Cfg<BM, WAVES_M, STAGES> C;
+    struct {
+        uint16_t a[STAGES][C::ASLICE];
+        uint16_t b[STAGES][BSLICE];
+    } ring;
+    Tables tab;
+};
+
+template <int MI, int NJ>
+struct Frags { bf16x8 a[MI]; bf16x8 b[NJ]; };
+
+// fragments of 16-wide k step s (0 or 1) of a slice; A fragments only for the first NB row
+// blocks, the ones that hold rows of the tile
+template <int MI, int NJ, int NB>
+__device__ inline void read_frags(Frags<MI, NJ>& f, const uint16_t* a, const uint16_t* b, int s, int r0, int c0) {
     const int l = threadIdx.x & 63, h = l >> 5;
     const int q = l >> 4, rr = (l >> 2) & 3, c = l & 3;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = *(const bf16x8*)(a + a_off(128 * wm + 32 * i + (l & 31), 2 * s + h));
+    for (int i = 0; i < NB; ++i) f.a[i] = *(const bf16x8*)(a + a_off(r0 + 32 * i + (l & 31), 2 * s + h));
     const int kr0 = 16 * s + 8 * (q >> 1) + rr;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int nn = 128 * wn + 32 * j + 16 * (q & 1) + 4 * c;
+    for (int j = 0; j < NJ; ++j) {
+        const int nn = c0 + 32 * j + 16 * (q & 1) + 4 * c;
         const i16x4 lo = lds_read_tr16(b + b_off(kr0, nn));
         const i16x4 hi = lds_read_tr16(b + b_off(kr0 + 4, nn));
         typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -87,18 +157,64 @@ __device__ inline void read_frags(Frags& f, const uint16_t* a, const uint16_t* b
     }
 }
 
-__device__ inline void mma(const Frags& f, f32x16 (&acc)[4][4]) {
+// acc[i][j] += B-fragment j x A-fragment i for the first NB row blocks
+template <int MI, int NJ, int NB>
+__device__ inline void mma(const Frags<MI, NJ>& f, f32x16 (&acc)[MI][NJ]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
-template <typename OutT>
+// calls f(std::integral_constant<int, I>) for I = B .. E - 1, in order
+template <int B, int E, typename F>
+__device__ inline void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// fragment read number R of k step s, in the order the MFMAs (column block major) first
+// need them: B block 0, A blocks 0 .. NB - 1, then B blocks 1 .. NJ - 1
+template <int MI, int NJ, int NB, int R>
+__device__ inline void read_one(Frags<MI, NJ>& f, const uint16_t* a, const uint16_t* b, int s, int r0, int c0) {
+    const int l = threadIdx.x & 63, h = l >> 5;
+    if constexpr (R >= 1 && R <= NB) {
+        f.a[R - 1] = *(const bf16x8*)(a + a_off(r0 + 32 * (R - 1) + (l & 31), 2 * s + h));
+    } else {
+        constexpr int j = R == 0 ? 0 : R - NB;
+        const int q = l >> 4, rr = (l >> 2) & 3, c = l & 3;
+        const int kr0 = 16 * s + 8 * (q >> 1) + rr;
+        const int nn = c0 + 32 * j + 16 * (q & 1) + 4 * c;
+        const i16x4 lo = lds_read_tr16(b + b_off(kr0, nn));
+        const i16x4 hi = lds_read_tr16(b + b_off(kr0 + 4, nn));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        f.b[j] = __builtin_bit_cast(bf16x8, v);
+    }
+}
+
+// calls fn(std::integral_constant<int, NB>) for the runtime value nb in [0, MAX]
+template <int MAX, typename F>
+__device__ inline void with_nb(int nb, F&& fn) {
+    if constexpr (MAX > 0) {
+        if (nb >= MAX) { fn(std::integral_constant<int, MAX>{}); return; }
+        with_nb<MAX - 1>(nb, fn);
+    } else {
+        fn(std::integral_constant<int, 0>{});
+    }
+}
+
+template <int BM, int WAVES_M, int STAGES, typename OutT>
 __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
-    __shared__ Smem sm;
-    const int t = threadIdx.x, l = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1, h = l >> 5;
+    typedef Cfg<BM, WAVES_M, STAGES> C;
+    constexpr int MI = C::MI, NJ = C::NJ;
+    __shared__ Smem<BM, WAVES_M, STAGES> sm;
+    const int t = threadIdx.x, l = t & 63, wave = t >> 6, h = l >> 5;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    const int r0w = wm * C::WROWS, c0w = wn * C::WCOLS;   // this wave's sub-tile origin
     const int ntn = cdiv(p.n, BN);
     int gemm_tiles, covered;
     if (p.uniform_rows > 0) {
@@ -114,35 +230,43 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
     const uint32_t k2 = (uint32_t)p.k * 2u, n2 = (uint32_t)p.n * 2u;
     constexpr int osz = sizeof(OutT);
 
-    // Ring-load roles (fixed per thread).  Wave w fills 1 KiB blocks 4w..4w+3 of each
-    // slice; lane l of block b writes LDS bytes [16 l, 16 l + 16) of it.
-    //   A block b = rows 16b..16b+15; lane l -> row 16b + l/4, physical chunk l%4, which
-    //     holds logical chunk (l%4) ^ ((row >> 2) & 3) = (l & 3) ^ ((l >> 4) & 3).
-    //   B block b = rows 2b, 2b+1; lane l -> row 2b + l/32, physical chunk l%32, which
-    //     holds logical chunk (l & 31) ^ b_swz(row).
-    const int a_chunk = (l & 3) ^ ((l >> 4) & 3);
-    int b_row[4], b_chunk[4];
+    // Ring-load roles (fixed per thread).  A slice: 1 KiB blocks of 16 rows, wave w fills
+    // blocks A_LOADS*w + u; lane l writes physical chunk l % 4 of row 16 b + l / 4, which
+    // holds logical chunk (l & 3) ^ ((row >> 1) & 3) = (l & 3) ^ ((l >> 3) & 3).
+    // B slice: 1 KiB blocks of 2 rows, wave w fills blocks 4w..4w+3; lane l writes
+    // physical chunk l % 32 of row 2b + l / 32, which holds logical chunk (l & 31) ^ b_swz.
+    const int a_chunk = (l & 3) ^ ((l >> 3) & 3);
+    // this wave's first 1 KiB block in A / B slot 0 (wave-uniform, scalar registers)
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds_a = lds_u32(&sm.ring.a[0][0]) + (uint32_t)(C::A_LOADS * wave_u) * 1024u;
+    const uint32_t lds_b = lds_u32(&sm.ring.b[0][0]) + (uint32_t)(4 * wave_u) * 1024u;
+    // per-lane parts of the ring-load offsets (the wave- and tile-uniform parts are added
+    // at each load, in scalar registers)
+    const uint32_t a_lane = (uint32_t)(l >> 2) * k2 + (uint32_t)a_chunk * 16u;
+    uint32_t b_lane[4];
+    int b_ch8[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        b_row[u] = 2 * (4 * wave + u) + (l >> 5);
-        b_chunk[u] = (l & 31) ^ b_swz(b_row[u]);
+        const int b_row = 2 * (4 * wave + u) + (l >> 5);
+        b_ch8[u] = 8 * ((l & 31) ^ b_swz(b_row));
+        b_lane[u] = (uint32_t)(l >> 5) * n2 + (uint32_t)b_ch8[u] * 2u;
     }
 
     for (int tile = xcd_virtual_id(blockIdx.x, gridDim.x); tile < total; tile += gridDim.x) {
         if (tile >= gemm_tiles) {   // rows past the covered ones: zeros, 16-byte stores
             const int z = tile - gemm_tiles;
-            const int r0 = covered + (z % zero_mt) * BM, c0 = (z / zero_mt) * BN;
-            const int rows = min(BM, p.m - r0);
-            const rsrc_t ro = make_rsrc((const char*)p.out + (size_t)r0 * p.n * osz, (uint32_t)(rows * p.n * osz));
+            const int zr0 = covered + (z % zero_mt) * BM, zc0 = (z / zero_mt) * BN;
+            const int rows = min(BM, p.m - zr0);
+            const rsrc_t ro = make_rsrc((const char*)p.out + (size_t)zr0 * p.n * osz, (uint32_t)(rows * p.n * osz));
             constexpr int per_row = BN * osz / 16;
             for (int idx = t; idx < BM * per_row; idx += NT) {
                 const int r = idx / per_row, cc = idx % per_row;
-                const int col = c0 + cc * (16 / osz);
+                const int col = zc0 + cc * (16 / osz);
                 bstore(ro, col < p.n ? (uint32_t)(r * p.n + col) * osz : kOOB, i32x4{0, 0, 0, 0});
             }
             continue;
         }
-        int grp, row0, size, local;
+        int grp, row0, size, local, mt, nt;
         if (p.uniform_rows > 0) {
             const int per = cdiv(p.uniform_rows, BM) * ntn;
             grp = tile / per; local = tile - grp * per; row0 = grp * p.uniform_rows; size = p.uniform_rows;
@@ -152,124 +276,169 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
             row0 = sm.tab.row_off[grp];
             size = sm.tab.row_off[grp + 1] - row0;
         }
+        // Within a group the tile that shares the streamed operand runs next (consecutive
+        // tiles land on one XCD): weights stream once per column when the group is short,
+        // rows stream once per row block when it is tall.  A group's partly filled last
+        // m-tile stays beside the full ones of its column, so its weight reads hit L2.
         const int mtg = cdiv(size, BM);
-        int mt, nt;
-        if (size <= p.n) { mt = local % mtg; nt = local / mtg; }   // weights stream once
-        else { nt = local % ntn; mt = local / ntn; }               // rows stream once
+        if (size <= p.n) { mt = local % mtg; nt = local / mtg; }
+        else { nt = local % ntn; mt = local / ntn; }
         row0 += mt * BM;
         const int rows_valid = min(BM, size - mt * BM);
         const int col0 = nt * BN;
+        // 32-row blocks of this wave that hold any of the tile's rows
+        const int nb = max(0, min(MI, cdiv(rows_valid - r0w, 32)));
 
-        const rsrc_t ra = make_rsrc((const uint16_t*)p.lhs + (size_t)row0 * p.k, (uint32_t)rows_valid * k2);
-        const rsrc_t rb = make_rsrc((const uint16_t*)p.rhs + (size_t)grp * p.k * p.n, (uint32_t)p.k * n2);
-        uint32_t a_voff[4], b_voff[4];
-        bool b_ok[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int row = 16 * (4 * wave + u) + (l >> 2);
-            a_voff[u] = (uint32_t)row * k2 + (uint32_t)a_chunk * 16u;
-            const int col = col0 + 8 * b_chunk[u];
-            b_ok[u] = col < p.n;
-            b_voff[u] = (uint32_t)b_row[u] * n2 + (uint32_t)col * 2u;
-        }
-        auto issue = [&](int stage) {
-            const int kk = stage * BK, slot = stage & (STAGES - 1);
-            const bool a_ok = kk + 8 * a_chunk < p.k;
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                load_lds16(ra, sm.ring.a[slot] + (4 * wave + u) * 512, a_ok ? a_voff[u] + (uint32_t)kk * 2u : kOOB);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                load_lds16(rb, sm.ring.b[slot] + (4 * wave + u) * 512, b_ok[u] ? b_voff[u] + (uint32_t)kk * n2 : kOOB);
+        const i32x4 ra = make_rsrc_v((const uint16_t*)p.lhs + (size_t)row0 * p.k, (uint32_t)rows_valid * k2);
+        const i32x4 rb = make_rsrc_v((const uint16_t*)p.rhs + (size_t)grp * p.k * p.n, (uint32_t)p.k * n2);
+        // ring load number d (A blocks first, then B) of k slice `stage` into its slot;
+        // slices past k are zero-filled into the slot no one reads, which keeps the number
+        // of loads per iteration, and so every wait count, constant
+        auto dma_one = [&](auto d_c, int stage) {
+            constexpr int d = decltype(d_c)::value;
+            const int kk = stage * BK, slot = stage % STAGES;
+            const bool live = stage < nk;
+            if constexpr (d < C::A_LOADS) {
+                // row 16 (A_LOADS wave + d) + l / 4 of the tile, chunk a_chunk
+                const bool ok = live && kk + 8 * a_chunk < p.k;
+                const uint32_t wpart = (uint32_t)(16 * (C::A_LOADS * wave_u + d)) * k2 + (uint32_t)kk * 2u;
+                load_lds16(ra, lds_a + (uint32_t)slot * (C::ASLICE * 2) + d * 1024u, ok ? a_lane + wpart : kOOB);
+            } else {
+                // k row kk + 2 (4 wave + u) + l / 32, columns col0 + b_ch8 .. + 7
+                constexpr int u = d - C::A_LOADS;
+                const bool ok = live && b_ch8[u] < p.n - col0;
+                const uint32_t wpart = (uint32_t)(kk + 2 * (4 * wave_u + u)) * n2 + (uint32_t)col0 * 2u;
+                load_lds16(rb, lds_b + (uint32_t)slot * (BSLICE * 2) + u * 1024u, ok ? b_lane[u] + wpart : kOOB);
+            }
         };
 
-        f32x16 acc[4][4];
+        f32x16 acc[MI][NJ];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-        Frags f0, f1;
-        if (nk > 0) {
-            const int pre = min(STAGES - 1, nk);
-            for (int s = 0; s < pre; ++s) issue(s);
-            wait_slices(pre - 1);
+        // One half slice: the MFMAs on `cur` with, after each, at most one ring load (of
+        // slice `stage`, when DMA) and one fragment read of `nxt` (k step s of slot a / b).
+        // The order is pinned so the loads and reads issue while the MFMAs run.
+        auto phase = [&](auto nb_c, auto dma_c, Frags<MI, NJ>& cur, Frags<MI, NJ>& nxt, const uint16_t* a,
+                         const uint16_t* b, int s, int stage) {
+            constexpr int NB = decltype(nb_c)::value;
+            constexpr bool DMA = decltype(dma_c)::value;
+            constexpr int NM = NB * NJ, NR = NB > 0 ? NB + NJ : 0, ND = DMA ? C::PER : 0;
+            constexpr int NOPS = NM > NR ? (NM > ND ? NM : ND) : (NR > ND ? NR : ND);
+            static_for<0, NOPS>([&](auto o_c) {
+                constexpr int o = decltype(o_c)::value;
+                if constexpr (o < NM) {   // column block major: block (o % NB, o / NB)
+                    constexpr int i = o % (NB > 0 ? NB : 1), j = o / (NB > 0 ? NB : 1);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
+                }
+                if constexpr (o < ND) dma_one(o_c, stage);
+                if constexpr (o < NR) read_one<MI, NJ, NB, o>(nxt, a, b, s, r0w, c0w);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+
+        auto run = [&](auto nb_c) {
+            constexpr int NB = decltype(nb_c)::value;
+            Frags<MI, NJ> f0, f1;
+            static_for<0, STAGES - 1>([&](auto st_c) { static_for<0, C::PER>([&](auto d_c) { dma_one(d_c, decltype(st_c)::value); }); });
+            // slice 0 in LDS.  Loads complete in issue order among themselves; output stores of
+            // the previous tile still in flight only raise the count, so this can only wait longer.
+            wait_vm<C::PER * (STAGES - 2)>();
             lds_barrier();
-            read_frags(f0, sm.ring.a[0], sm.ring.b[0], 0, wm, wn);
-        }
-        for (int kt = 0; kt < nk; ++kt) {
-            const int slot = kt & (STAGES - 1);
-            if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
-            read_frags(f1, sm.ring.a[slot], sm.ring.b[slot], 1, wm, wn);
-            mma(f0, acc);
-            if (kt + 1 < nk) {
-                wait_slices(min(nk - 1, kt + STAGES - 1) - (kt + 1));
+            if constexpr (NB > 0) read_frags<MI, NJ, NB>(f0, sm.ring.a[0], sm.ring.b[0], 0, r0w, c0w);
+            for (int kt = 0; kt + 1 < nk; ++kt) {
+                const int slot = kt % STAGES, ns = (kt + 1) % STAGES;
+                phase(nb_c, std::true_type{}, f0, f1, sm.ring.a[slot], sm.ring.b[slot], 1, kt + STAGES - 1);
+                wait_vm<C::PER * (STAGES - 2)>();   // slice kt + 1 in LDS
                 lds_barrier();
-                const int ns = (kt + 1) & (STAGES - 1);
-                read_frags(f0, sm.ring.a[ns], sm.ring.b[ns], 0, wm, wn);
+                phase(nb_c, std::false_type{}, f1, f0, sm.ring.a[ns], sm.ring.b[ns], 0, 0);
             }
-            mma(f1, acc);
-        }
+            const int last = (nk - 1) % STAGES;
+            phase(nb_c, std::false_type{}, f0, f1, sm.ring.a[last], sm.ring.b[last], 1, 0);
+            mma<MI, NJ, NB>(f1, acc);
+        };
+        if (nk > 0) with_nb<MI>(nb, run);
         lds_barrier();   // every wave is done with the ring before it is reused
 
-        // epilogue: acc[i][j][4q + e] = C[128wm + 32i + (l & 31)][128wn + 32j + 8q + 4h + e]
+        // epilogue: acc[i][j][4q + e] = C[r0w + 32i + (l & 31)][c0w + 32j + 8q + 4h + e]
         const rsrc_t ro = make_rsrc((const char*)p.out + (size_t)row0 * p.n * osz, (uint32_t)(rows_valid * p.n * osz));
         if constexpr (osz == 2) {
-            const int m_l = 128 * wm + (l & 31);
+            // Through a wave-private fp32 strip in the (now idle) ring: the accumulators go
+            // to LDS straight from AGPRs, come back 8 consecutive columns per lane, and leave
+            // as 16-byte bf16 stores, a whole 2 * WCOLS-byte row segment per WCOLS / 8 lanes.
+            // (Converting in place would copy every accumulator through VGPRs.)  Row pitch
+            // WCOLS + 4 floats spreads the 32 rows one write touches over all banks.
+            constexpr int SP = C::WCOLS + 4, LPR = C::WCOLS / 8, RPS = 64 / LPR;
+            static_assert(4 * 32 * SP * 4 <= (int)sizeof(sm.ring), "staging strip fits the ring");
+            float* st = reinterpret_cast<float*>(&sm.ring) + wave * 32 * SP;
+            const int rr = l / LPR, g = l % LPR;
+            const int col = col0 + c0w + 8 * g;
+            const uint32_t col_ok = col < p.n;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < MI; ++i) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < NJ; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                        bf16x4 v = {(__bf16)acc[i][j][4 * q], (__bf16)acc[i][j][4 * q + 1], (__bf16)acc[i][j][4 * q + 2],
-                                    (__bf16)acc[i][j][4 * q + 3]};
-                        const int n_l = 128 * wn + 32 * j + 8 * q + 4 * h;
-                        *(bf16x4*)(sm.c + (m_l + 32 * i) * CP + n_l) = v;
+                        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                        *(f32x4*)(st + (l & 31) * SP + 32 * j + 8 * q + 4 * h) = v;
                     }
-            lds_barrier();
-            const int cc = t & 31;
-            const int col = col0 + cc * 8;
-#pragma unroll 4
-            for (int it = 0; it < BM / 8; ++it) {
-                const int r = it * 8 + (t >> 5);
-                const i32x4 v = *(const i32x4*)(sm.c + r * CP + cc * 8);
-                bstore(ro, col < p.n ? (uint32_t)(r * p.n + col) * 2u : kOOB, v);
+#pragma unroll
+                for (int t2 = 0; t2 < 32 / RPS; ++t2) {
+                    const int rs = t2 * RPS + rr;   // row within the strip
+                    const f32x4 lo = *(const f32x4*)(st + rs * SP + 8 * g);
+                    const f32x4 hi = *(const f32x4*)(st + rs * SP + 8 * g + 4);
+                    const i32x4 v = {(int)pack_bf16(lo[0], lo[1]), (int)pack_bf16(lo[2], lo[3]), (int)pack_bf16(hi[0], hi[1]),
+                                     (int)pack_bf16(hi[2], hi[3])};
+                    const int r = r0w + 32 * i + rs;
+                    bstore(ro, col_ok ? (uint32_t)(r * p.n + col) * 2u : kOOB, v);
+                }
             }
-            lds_barrier();
+            lds_barrier();   // strips read before the next tile's ring loads land there
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < NJ; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const int r = 128 * wm + 32 * i + (l & 31);
-                        const int col = col0 + 128 * wn + 32 * j + 8 * q + 4 * h;
+                        const int r = r0w + 32 * i + (l & 31);
+                        const int col = col0 + c0w + 32 * j + 8 * q + 4 * h;
                         const i32x4 v = {__float_as_int(acc[i][j][4 * q]), __float_as_int(acc[i][j][4 * q + 1]),
                                          __float_as_int(acc[i][j][4 * q + 2]), __float_as_int(acc[i][j][4 * q + 3])};
                         bstore(ro, col < p.n ? (uint32_t)(r * p.n + col) * 4u : kOOB, v);
                     }
         }
     }
+    wait_vm<0>();   // no ring load may still be writing LDS when the workgroup ends
 }
 
-}  // namespace mb3
+// tile shape: (rows, waves along rows, ring slots).  256 x 256 with a 4-slot ring is the
+// fastest of the shapes the template allows (64 / 128 / 256 rows, 1 / 2 / 4 row waves, 3-7
+// slots) both on groups of ~1000 rows, where the MFMA bounds it, and on Zipf-skewed groups
+// of ~128 rows, where the weight stream does: blocks past a group's last row are skipped,
+// so tall tiles cost short groups little, while they halve the B fragment reads per flop.
+#define GG_TILE 256, 2, 4
+
+}  // namespace mb
+
+int ragged_m_bf16_fast_bm(const MParams&) { return mb::Cfg<GG_TILE>::BM_ROWS; }
 
 bool ragged_m_bf16_fast_ok(const MParams& p) {
     // 32-bit buffer offsets: one expert's weights and one tile's rows must fit in 2 GiB
     const uint64_t w = (uint64_t)p.k * (uint64_t)p.n * 2u;
-    const uint64_t a = (uint64_t)mb3::BM * (uint64_t)p.k * 2u;
-    const uint64_t o = (uint64_t)mb3::BM * (uint64_t)p.n * 4u;
+    const uint64_t a = 256ull * (uint64_t)p.k * 2u;
+    const uint64_t o = 256ull * (uint64_t)p.n * 4u;
     return p.k % 8 == 0 && p.n % 8 == 0 && w < (1ull << 31) && a < (1ull << 31) && o < (1ull << 31);
 }
 
 hipError_t launch_ragged_m_bf16_fast(const MParams& p, int grid, hipStream_t s) {
-    if (p.out_f32) hipLaunchKernelGGL((mb3::kernel<float>), dim3(grid), dim3(mb3::NT), 0, s, p);
-    else hipLaunchKernelGGL((mb3::kernel<uint16_t>), dim3(grid), dim3(mb3::NT), 0, s, p);
+    if (p.out_f32) hipLaunchKernelGGL((mb::kernel<GG_TILE, float>), dim3(grid), dim3(mb::NT), 0, s, p);
+    else hipLaunchKernelGGL((mb::kernel<GG_TILE, uint16_t>), dim3(grid), dim3(mb::NT), 0, s, p);
     return hipGetLastError();
 }
 
