@@ -44,6 +44,11 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 3 times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="no GPU work: read rocprofv3 --pmc outputs under DIR (fetch_<workload>, "
+                         "write_<workload>, copy_fetch, copy_write) and record the HBM bytes per launch "
+                         "of each workload's dominant kernel in profiles/traffic.json")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30, help="byte count the copy probe was run with")
     return ap.parse_args()
 
 
@@ -121,19 +126,88 @@ def cpu_baseline(w, d, gs, target_s, W, torch):
             "sample": f"{done} {unit} of the {w.name} workload drawn uniformly, fp64 oracle, {spent:.1f} s"}
 
 
+def kernels_digest():
+    """sha256 over the kernel sources; a traffic record taken from other sources is stale."""
+    import hashlib
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "group_gemm_amd", "csrc")
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(d)):
+        if fn.endswith((".hip", ".hpp", ".h")):
+            h.update(fn.encode())
+            with open(os.path.join(d, fn), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
 def traffic_for(name):
-    """HBM bytes per launch measured with rocprofv3 counters for the current kernel build,
-    if such a measurement is on file."""
+    """HBM bytes per launch of the workload's dominant kernel, measured with rocprofv3
+    counters on the current kernel sources; None when there is no such measurement."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             rec = json.load(f).get(name)
-        return None if rec is None else rec.get("bytes_per_launch")
     except (OSError, ValueError):
         return None
+    if rec is None or rec.get("kernels_sha256") != kernels_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def _pmc_rows(path, counter):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    out = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def ingest_traffic(a):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each workload's dominant library kernel,
+    scaled by what the same counters read for a plain copy of a known size."""
+    d = a.traffic_from
+    copy = {}
+    for ctr, sub in (("FETCH_SIZE", "copy_fetch"), ("WRITE_SIZE", "copy_write")):
+        rows = _pmc_rows(os.path.join(d, sub), ctr)
+        vals = [v for k, vs in rows.items() if "copyBuffer" in k for v in vs]
+        copy[ctr] = a.copy_bytes / (sum(vals) / len(vals) * 1024.0)
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    digest = kernels_digest()
+    for sub in sorted(os.listdir(d)):
+        if not sub.startswith("fetch_") or not os.path.isdir(os.path.join(d, sub)):
+            continue
+        wl = sub[len("fetch_"):]
+        per = {}
+        for ctr, pre in (("FETCH_SIZE", "fetch_"), ("WRITE_SIZE", "write_")):
+            rows = _pmc_rows(os.path.join(d, pre + wl), ctr)
+            ours = {k: v for k, v in rows.items() if k.startswith("void gg::")}
+            kern = max(ours, key=lambda k: sum(ours[k]))
+            per[ctr] = (kern, sum(ours[kern]) / len(ours[kern]) * 1024.0 * copy[ctr], len(ours[kern]))
+        table[wl] = {"kernel": per["FETCH_SIZE"][0], "dispatches": per["FETCH_SIZE"][2],
+                     "fetch_bytes": per["FETCH_SIZE"][1], "write_bytes": per["WRITE_SIZE"][1],
+                     "bytes_per_launch": per["FETCH_SIZE"][1] + per["WRITE_SIZE"][1],
+                     "fetch_factor": copy["FETCH_SIZE"], "write_factor": copy["WRITE_SIZE"],
+                     "kernels_sha256": digest}
+        print(wl, json.dumps(table[wl]))
+    with open(PROFILE_TRAFFIC, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+        f.write("\n")
 
 
 def main():
     a = parse()
+    if a.traffic_from:
+        ingest_traffic(a)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path would shard by "
               "experts or tokens, see the design notes).", file=sys.stderr)

@@ -80,10 +80,14 @@ gg_status run_m(const void* lhs, const void* rhs, const int32_t* gs, void* out, 
         if (fast) e = gg::launch_ragged_m_bf16_fast(p, persistent_grid(bound, 1, cus), s);
         else e = gg::launch_ragged_m_bf16(p, persistent_grid(bound, 1, cus), vec, s);
     } else {
+        const bool fast = aligned(lhs, 16) && aligned(rhs, 16) && aligned(out, 16) && aligned(ls, 4) && aligned(rs, 4) &&
+                          gg::ragged_m_mx_fast_ok(p);
         gg::TileShape ts = gg::tiles_m_e4m3();
+        if (fast) ts = {256, 256};
         int64_t bound = (cdiv64(m, ts.bm) + g + 1) * cdiv64(n, ts.bn);
         if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
-        e = gg::launch_ragged_m_e4m3(p, persistent_grid(bound, 1, cus), s);
+        if (fast) e = gg::launch_ragged_m_mx_fast(p, persistent_grid(bound, 1, cus), s);
+        else e = gg::launch_ragged_m_e4m3(p, persistent_grid(bound, 1, cus), s);
     }
     return e == hipSuccess ? GG_OK : GG_ERR_HIP;
 }

@@ -42,6 +42,10 @@ int ragged_m_bf16_fast_bm(const MParams& p);   // tile rows the vectorised kerne
 hipError_t launch_ragged_m_bf16_fast(const MParams& p, int grid, hipStream_t s);
 hipError_t launch_ragged_m_f32(const MParams& p, int grid, hipStream_t s);
 hipError_t launch_ragged_m_e4m3(const MParams& p, int grid, hipStream_t s);
+// MXFP8 ring kernel (16-byte aligned operands and output, 4-byte aligned scales,
+// k % 128 == 0, n % 16 == 0); 256 x 256 tiles
+bool ragged_m_mx_fast_ok(const MParams& p);
+hipError_t launch_ragged_m_mx_fast(const MParams& p, int grid, hipStream_t s);
 hipError_t launch_ragged_k_bf16(const KParams& p, int grid, bool vec, hipStream_t s);
 hipError_t launch_ragged_k_f32(const KParams& p, int grid, hipStream_t s);
 

@@ -28,79 +28,16 @@
 //  * The MFMA takes the weight fragment as its first operand, which gives every lane 4
 //    consecutive output columns; fp32 results are stored straight from AGPRs, bf16
 //    results pass through a wave-private fp32 strip in LDS (see the epilogue).
-#include <type_traits>
-
 #include "common.hpp"
 #include "launch.hpp"
+#include "ring.hpp"
 
 namespace gg {
 namespace mb {
+using namespace ring;
 
 constexpr int BN = 256, BK = 32, NT = 256;
 constexpr int BSLICE = BK * BN;          // elements of one B slice: 16 KiB
-constexpr uint32_t kOOB = 0x80000000u;   // a buffer offset past every num_records
-constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
-}
-// the same descriptor as four scalar registers, for the inline-asm ring loads
-__device__ inline i32x4 make_rsrc_v(const void* base, uint32_t bytes) {
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    i32x4 r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-    r[3] = kRsrcWord3;
-    return r;
-}
-__device__ inline void bstore(rsrc_t r, uint32_t off, i32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0); }
-// two floats -> two bf16 (round to nearest even), low element in the low half
-__device__ inline uint32_t pack_bf16(float a, float b) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 v = {(__bf16)a, (__bf16)b};
-    return __builtin_bit_cast(uint32_t, v);
-}
-// 16 bytes per lane from the buffer straight into LDS at lds + 16 * lane.  Issued from
-// inline asm so the compiler does not track it as an LDS write: its alias rule would make
-// every LDS read wait for all outstanding loads.  The kernel orders these loads itself
-// (explicit vmcnt waits, then a barrier) and issues no other vector-memory loads while
-// the ring is running, so the counts it waits on are exact.
-// lds_addr is a wave-uniform LDS byte address.
-__device__ inline void load_lds16(i32x4 r, uint32_t lds_addr, uint32_t off) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(lds_addr), "v"(off), "s"(r) : "memory", "m0");
-}
-// LDS byte address of a pointer into a __shared__ object
-__device__ inline uint32_t lds_u32(const void* p) {
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-}
-// barrier that waits for this wave's LDS accesses only; ring loads stay in flight.  The
-// builtin wait tells the compiler's own wait tracking that LDS reads issued before the
-// barrier are complete (it cannot see into the asm, and would otherwise make later
-// MFMAs wait on reads they do not use); the asm keeps the wait and the barrier together.
-__device__ inline void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt and expcnt at their maximum: no wait
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-// wait until at most N vector-memory operations of this thread are outstanding
-template <int N>
-__device__ inline void wait_vm() {
-    static_assert(N >= 0 && N <= 63, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-// wait until at most `later` slices (PER operations each) are still in flight
-template <int PER, int MAXL>
-__device__ inline void wait_slices(int later) {
-    if constexpr (MAXL > 0) {
-        if (later >= MAXL) { wait_vm<PER * MAXL>(); return; }
-        wait_slices<PER, MAXL - 1>(later);
-    } else {
-        wait_vm<0>();
-    }
-}
 
 // B slice [32 k][256 n], 512-byte rows: 16-byte chunks XOR'ed in 64-byte units by a 3-bit
 // function of the row, so the rows one transpose read touches land in distinct bank groups.
@@ -167,14 +104,6 @@ __device__ inline void mma(const Frags<MI, NJ>& f, f32x16 (&acc)[MI][NJ]) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
-// calls f(std::integral_constant<int, I>) for I = B .. E - 1, in order
-template <int B, int E, typename F>
-__device__ inline void static_for(F&& f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E>(f);
-    }
-}
 
 // fragment read number R of k step s, in the order the MFMAs (column block major) first
 // need them: B block 0, A blocks 0 .. NB - 1, then B blocks 1 .. NJ - 1
@@ -196,16 +125,6 @@ __device__ inline void read_one(Frags<MI, NJ>& f, const uint16_t* a, const uint1
     }
 }
 
-// calls fn(std::integral_constant<int, NB>) for the runtime value nb in [0, MAX]
-template <int MAX, typename F>
-__device__ inline void with_nb(int nb, F&& fn) {
-    if constexpr (MAX > 0) {
-        if (nb >= MAX) { fn(std::integral_constant<int, MAX>{}); return; }
-        with_nb<MAX - 1>(nb, fn);
-    } else {
-        fn(std::integral_constant<int, 0>{});
-    }
-}
 
 template <int BM, int WAVES_M, int STAGES, typename OutT>
 __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
@@ -253,17 +172,9 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
     }
 
     for (int tile = xcd_virtual_id(blockIdx.x, gridDim.x); tile < total; tile += gridDim.x) {
-        if (tile >= gemm_tiles) {   // rows past the covered ones: zeros, 16-byte stores
+        if (tile >= gemm_tiles) {   // rows past the covered ones: zeros
             const int z = tile - gemm_tiles;
-            const int zr0 = covered + (z % zero_mt) * BM, zc0 = (z / zero_mt) * BN;
-            const int rows = min(BM, p.m - zr0);
-            const rsrc_t ro = make_rsrc((const char*)p.out + (size_t)zr0 * p.n * osz, (uint32_t)(rows * p.n * osz));
-            constexpr int per_row = BN * osz / 16;
-            for (int idx = t; idx < BM * per_row; idx += NT) {
-                const int r = idx / per_row, cc = idx % per_row;
-                const int col = zc0 + cc * (16 / osz);
-                bstore(ro, col < p.n ? (uint32_t)(r * p.n + col) * osz : kOOB, i32x4{0, 0, 0, 0});
-            }
+            zero_tile<BM, BN, NT, OutT>(p.out, covered + (z % zero_mt) * BM, p.m, (z / zero_mt) * BN, p.n);
             continue;
         }
         int grp, row0, size, local, mt, nt;
@@ -364,55 +275,10 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
         if (nk > 0) with_nb<MI>(nb, run);
         lds_barrier();   // every wave is done with the ring before it is reused
 
-        // epilogue: acc[i][j][4q + e] = C[r0w + 32i + (l & 31)][c0w + 32j + 8q + 4h + e]
         const rsrc_t ro = make_rsrc((const char*)p.out + (size_t)row0 * p.n * osz, (uint32_t)(rows_valid * p.n * osz));
-        if constexpr (osz == 2) {
-            // Through a wave-private fp32 strip in the (now idle) ring: the accumulators go
-            // to LDS straight from AGPRs, come back 8 consecutive columns per lane, and leave
-            // as 16-byte bf16 stores, a whole 2 * WCOLS-byte row segment per WCOLS / 8 lanes.
-            // (Converting in place would copy every accumulator through VGPRs.)  Row pitch
-            // WCOLS + 4 floats spreads the 32 rows one write touches over all banks.
-            constexpr int SP = C::WCOLS + 4, LPR = C::WCOLS / 8, RPS = 64 / LPR;
-            static_assert(4 * 32 * SP * 4 <= (int)sizeof(sm.ring), "staging strip fits the ring");
-            float* st = reinterpret_cast<float*>(&sm.ring) + wave * 32 * SP;
-            const int rr = l / LPR, g = l % LPR;
-            const int col = col0 + c0w + 8 * g;
-            const uint32_t col_ok = col < p.n;
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-#pragma unroll
-                for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                        *(f32x4*)(st + (l & 31) * SP + 32 * j + 8 * q + 4 * h) = v;
-                    }
-#pragma unroll
-                for (int t2 = 0; t2 < 32 / RPS; ++t2) {
-                    const int rs = t2 * RPS + rr;   // row within the strip
-                    const f32x4 lo = *(const f32x4*)(st + rs * SP + 8 * g);
-                    const f32x4 hi = *(const f32x4*)(st + rs * SP + 8 * g + 4);
-                    const i32x4 v = {(int)pack_bf16(lo[0], lo[1]), (int)pack_bf16(lo[2], lo[3]), (int)pack_bf16(hi[0], hi[1]),
-                                     (int)pack_bf16(hi[2], hi[3])};
-                    const int r = r0w + 32 * i + rs;
-                    bstore(ro, col_ok ? (uint32_t)(r * p.n + col) * 2u : kOOB, v);
-                }
-            }
-            lds_barrier();   // strips read before the next tile's ring loads land there
-        } else {
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int r = r0w + 32 * i + (l & 31);
-                        const int col = col0 + c0w + 32 * j + 8 * q + 4 * h;
-                        const i32x4 v = {__float_as_int(acc[i][j][4 * q]), __float_as_int(acc[i][j][4 * q + 1]),
-                                         __float_as_int(acc[i][j][4 * q + 2]), __float_as_int(acc[i][j][4 * q + 3])};
-                        bstore(ro, col < p.n ? (uint32_t)(r * p.n + col) * 4u : kOOB, v);
-                    }
-        }
+        static_assert(4 * 32 * (C::WCOLS + 4) * 4 <= (int)sizeof(sm.ring), "epilogue strips fit the ring");
+        store_acc<MI, NJ, C::WCOLS, OutT>(acc, reinterpret_cast<float*>(&sm.ring) + wave * 32 * (C::WCOLS + 4), ro, p.n, col0, r0w, c0w);
+        if constexpr (osz == 2) lds_barrier();   // strips read before the next tile's ring loads land there
     }
     wait_vm<0>();   // no ring load may still be writing LDS when the workgroup ends
 }

@@ -163,6 +163,37 @@ def test_ragged_m_mxfp8_small(case):
     assert torch.all(y[sum(gs):] == 0)
 
 
+# Shapes on the 16-byte / 4-byte ring path of the MXFP8 kernel (k % 128 == 0, n % 16 == 0):
+# one to sixteen 64-wide k slices (fewer than the ring's prefetch depth included), ragged
+# and empty groups, a group spanning three 256-row tiles with an 8-row tail, partial
+# 256-column tiles.
+MX_RING_CASES = [
+    (600, 512, 400, [0, 37, 256, 1, 300, 6]),
+    (520, 1024, 272, [520]),
+    (257, 128, 256, [128, 129]),
+    (96, 384, 512, [32, 0, 64]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(MX_RING_CASES)))
+def test_ragged_m_mxfp8_ring(case):
+    m, k, n, gs = MX_RING_CASES[case]
+    say("ragged_m mxfp8 ring", m, k, n, len(gs))
+    d = to_dev(W.small_inputs("m", "mxfp8", m, k, n, gs, seed=40 + case))
+    ref = oracle_m(d)
+    y = run_m(d)
+    check_bf16(y, ref, f"mx ring case {case}")
+    assert torch.all(y[sum(gs):] == 0)
+    if case < 2:
+        # an MXFP8 product stored as fp32 is held to the MXFP8 bar; its normwise error is
+        # also bounded by fp32 accumulation of k block-scaled products (~sqrt(k) 2^-24 times
+        # the sum's condition number), well under 1e-4 here
+        y32 = run_m(d, out_dtype=torch.float32)
+        check_bf16(y32, ref, f"mx ring case {case}, fp32 out")
+        y32 = y32.double().cpu().numpy()
+        assert np.linalg.norm(y32 - ref) <= 1e-4 * np.linalg.norm(ref), f"mx ring case {case}, fp32 out, normwise"
+
+
 def test_device_status_and_clamping():
     say("invalid group sizes")
     m, k, n = 200, 64, 64
