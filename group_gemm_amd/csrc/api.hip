@@ -111,7 +111,9 @@ gg_status run_k(const void* lhs, const void* dout, const int32_t* gs, void* out,
         int64_t bound = (int64_t)g * cdiv64(k, ts.bm) * cdiv64(n, ts.bn);
         if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
         const bool vec = aligned(lhs, 16) && aligned(dout, 16) && k % 8 == 0 && n % 8 == 0;
-        e = gg::launch_ragged_k_bf16(p, persistent_grid(bound, 1, cus), vec, s);
+        if (vec && aligned(out, 16) && gg::ragged_k_bf16_fast_ok(p))
+            e = gg::launch_ragged_k_bf16_fast(p, persistent_grid(bound, 1, cus), s);
+        else e = gg::launch_ragged_k_bf16(p, persistent_grid(bound, 1, cus), vec, s);
     }
     return e == hipSuccess ? GG_OK : GG_ERR_HIP;
 }

@@ -47,6 +47,9 @@ hipError_t launch_ragged_m_e4m3(const MParams& p, int grid, hipStream_t s);
 bool ragged_m_mx_fast_ok(const MParams& p);
 hipError_t launch_ragged_m_mx_fast(const MParams& p, int grid, hipStream_t s);
 hipError_t launch_ragged_k_bf16(const KParams& p, int grid, bool vec, hipStream_t s);
+// contracting ring kernel (16-byte aligned operands and output, k % 8 == 0, n % 8 == 0)
+bool ragged_k_bf16_fast_ok(const KParams& p);
+hipError_t launch_ragged_k_bf16_fast(const KParams& p, int grid, hipStream_t s);
 hipError_t launch_ragged_k_f32(const KParams& p, int grid, hipStream_t s);
 
 // Static tile geometry of each family (host-side grid sizing).

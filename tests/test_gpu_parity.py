@@ -218,6 +218,8 @@ K_CASES = [
     (700, 264, 128, [1, 255, 256, 150, 0, 1]),   # sum < m: trailing rows ignored
     (100, 72, 100, [30, 30, 40]),                 # unaligned -> element-wise path
     (64, 256, 256, [0, 0, 0, 0]),                 # all groups empty
+    (2048, 640, 1280, [700, 0, 1, 1000, 347]),    # many row slices; 3 x 5 tiles per group
+    (1100, 256, 2304, [90, 0, 200, 33, 64, 1, 150, 100, 2, 300, 60, 100]),   # 9 n-tiles: 8-wide super-tile + 1
 ]
 
 
