@@ -37,6 +37,7 @@ def lib():
         L.gg_workspace_bytes.restype = sz
         L.ragged_dot_m.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
         L.ragged_dot_k.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, ctypes.c_int, vp, sz, vp]
+        L.ragged_dot_m_nk.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, ctypes.c_int, vp, sz, vp]
         L.padded_dot.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i32, i64, ctypes.c_int, ctypes.c_int,
                                  vp, vp, vp, sz, vp]
         L.gg_schedule.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
@@ -44,7 +45,7 @@ def lib():
         L.gg_status_string.argtypes = [ctypes.c_int]
         L.gg_status_string.restype = ctypes.c_char_p
         L.gg_abi_version.restype = ctypes.c_int
-        for f in ("ragged_dot_m", "ragged_dot_k", "padded_dot", "gg_schedule", "gg_read_device_status"):
+        for f in ("ragged_dot_m", "ragged_dot_m_nk", "ragged_dot_k", "padded_dot", "gg_schedule", "gg_read_device_status"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -84,12 +85,19 @@ def _workspace(op, m, k, n, g, capacity, in_dtype, device, workspace):
     return workspace
 
 
-def ragged_dot_m(lhs, rhs, group_sizes, out=None, out_dtype=None, lhs_scale=None, rhs_scale=None, workspace=None):
+def ragged_dot_m(lhs, rhs, group_sizes, out=None, out_dtype=None, lhs_scale=None, rhs_scale=None, workspace=None,
+                 rhs_layout="kn"):
     """out[m,n]: row block of group h of lhs [m,k] times rhs[h] [k,n]; rows past
     sum(group_sizes) are 0.  e4m3 inputs (uint8 codes) need E8M0 lhs_scale [m,k/32] and
-    rhs_scale [g,k/32,n]."""
+    rhs_scale [g,k/32,n].  rhs_layout="nk" takes rhs as [g,n,k] (k contiguous) and
+    multiplies by rhs[h]^T: the data-gradient classes, bf16 only (ragged_dot_m_nk)."""
     m, k = lhs.shape
-    g, k2, n = rhs.shape
+    if rhs_layout == "nk":
+        g, n, k2 = rhs.shape
+    elif rhs_layout == "kn":
+        g, k2, n = rhs.shape
+    else:
+        raise ValueError(f"rhs_layout must be 'kn' or 'nk', not {rhs_layout!r}")
     if k2 != k or group_sizes.shape != (g,) or group_sizes.dtype != torch.int32:
         raise ValueError("shape/dtype mismatch")
     if out_dtype is None:
@@ -97,6 +105,13 @@ def ragged_dot_m(lhs, rhs, group_sizes, out=None, out_dtype=None, lhs_scale=None
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=lhs.device)
     ws = _workspace("ragged_m", m, k, n, g, 0, lhs.dtype, lhs.device, workspace)
+    if rhs_layout == "nk":
+        if lhs_scale is not None or rhs_scale is not None:
+            raise ValueError("rhs_layout='nk' takes no scales")
+        code = lib().ragged_dot_m_nk(_p(lhs), _p(rhs), _p(group_sizes), _p(out), m, k, n, g, GG_DT[lhs.dtype],
+                                     GG_DT[out.dtype], _p(ws), ws.numel(), _stream(lhs.device))
+        _check(code, "ragged_dot_m_nk")
+        return out
     code = lib().ragged_dot_m(_p(lhs), _p(rhs), _p(group_sizes), _p(out), m, k, n, g, GG_DT[lhs.dtype],
                               GG_DT[out.dtype], _p(lhs_scale), _p(rhs_scale), _p(ws), ws.numel(),
                               _stream(lhs.device))

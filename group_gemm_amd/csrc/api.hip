@@ -57,15 +57,22 @@ gg_status check_common(int64_t m, int64_t k, int64_t n, int32_t g, const int32_t
 // ragged_dot_m body, shared with the batched stage of padded_dot (uniform_rows > 0).
 gg_status run_m(const void* lhs, const void* rhs, const int32_t* gs, void* out, int64_t m, int64_t k, int64_t n,
                 int32_t g, gg_dtype in, gg_dtype outd, const uint8_t* ls, const uint8_t* rs, uint32_t* status,
-                int uniform_rows, hipStream_t s) {
+                int uniform_rows, hipStream_t s, bool rhs_nk = false) {
     int cus;
     if (device_cus(&cus) != 0) return GG_ERR_HIP;
     gg::MParams p{};
     p.lhs = lhs; p.rhs = rhs; p.lhs_scale = ls; p.rhs_scale = rs; p.group_sizes = gs; p.out = out; p.status = status;
     p.m = (int)m; p.k = (int)k; p.n = (int)n; p.g = g; p.uniform_rows = uniform_rows;
     p.out_f32 = outd == GG_DT_F32;
+    p.rhs_nk = rhs_nk ? 1 : 0;
     hipError_t e;
-    if (in == GG_DT_F32) {
+    if (rhs_nk) {   // [g,n,k] weights: the bf16 ring kernel only
+        const bool vec = aligned(lhs, 16) && aligned(rhs, 16) && aligned(out, 16) && k % 8 == 0 && n % 8 == 0;
+        if (in != GG_DT_BF16 || !vec || !gg::ragged_m_bf16_fast_ok(p)) return GG_ERR_UNSUPPORTED;
+        int64_t bound = (cdiv64(m, gg::ragged_m_bf16_fast_bm(p)) + g + 1) * cdiv64(n, 256);
+        if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
+        e = gg::launch_ragged_m_bf16_fast(p, persistent_grid(bound, 1, cus), s);
+    } else if (in == GG_DT_F32) {
         gg::TileShape ts = gg::tiles_m_f32();
         int64_t bound = (cdiv64(m, ts.bm) + g + 1) * cdiv64(n, ts.bn);
         if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
@@ -189,6 +196,20 @@ gg_status ragged_dot_m(const void* lhs, const void* rhs, const int32_t* group_si
     }
     return run_m(lhs, rhs, group_sizes, out, m, k, n, g, in_dtype, out_dtype, lhs_scale, rhs_scale, (uint32_t*)workspace,
                  0, (hipStream_t)stream);
+}
+
+gg_status ragged_dot_m_nk(const void* lhs, const void* rhs_nk, const int32_t* group_sizes, void* out, int64_t m,
+                          int64_t k, int64_t n, int32_t g, gg_dtype in_dtype, gg_dtype out_dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    gg_status st = check_common(m, k, n, g, group_sizes, workspace, workspace_bytes, kHeader);
+    if (st != GG_OK) return st;
+    if (in_dtype != GG_DT_BF16) return GG_ERR_UNSUPPORTED;
+    if (!m_dtypes_ok(in_dtype, out_dtype)) return GG_ERR_BAD_DTYPE;
+    if ((m * k > 0 && !lhs) || (k * n > 0 && !rhs_nk) || (m * n > 0 && !out)) return GG_ERR_NULL_PTR;
+    if (!aligned(lhs, 16) || !aligned(rhs_nk, 16) || !aligned(out, 16)) return GG_ERR_MISALIGNED;
+    if (k % 8 != 0 || n % 8 != 0) return GG_ERR_UNSUPPORTED;
+    return run_m(lhs, rhs_nk, group_sizes, out, m, k, n, g, in_dtype, out_dtype, nullptr, nullptr, (uint32_t*)workspace,
+                 0, (hipStream_t)stream, true);
 }
 
 gg_status ragged_dot_k(const void* lhs, const void* dout, const int32_t* group_sizes, void* out, int64_t m, int64_t k,

@@ -20,6 +20,7 @@ struct MParams {
     int m, k, n, g;
     int uniform_rows;           // > 0: every group has exactly this many rows (batched form)
     int out_f32;                // 1: fp32 output, 0: bf16 output
+    int rhs_nk;                 // 1: rhs is [g,n,k] (k contiguous; the dgrad classes), 0: [g,k,n]
 };
 
 // Contracting ragged dot: out[g,k,n] = per-group lhs[rows,k]^T . dout[rows,n].

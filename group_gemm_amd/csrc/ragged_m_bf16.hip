@@ -74,26 +74,6 @@ struct Smem {
 template <int MI, int NJ>
 struct Frags { bf16x8 a[MI]; bf16x8 b[NJ]; };
 
-// fragments of 16-wide k step s (0 or 1) of a slice; A fragments only for the first NB row
-// blocks, the ones that hold rows of the tile
-template <int MI, int NJ, int NB>
-__device__ inline void read_frags(Frags<MI, NJ>& f, const uint16_t* a, const uint16_t* b, int s, int r0, int c0) {
-    const int l = threadIdx.x & 63, h = l >> 5;
-    const int q = l >> 4, rr = (l >> 2) & 3, c = l & 3;
-#pragma unroll
-    for (int i = 0; i < NB; ++i) f.a[i] = *(const bf16x8*)(a + a_off(r0 + 32 * i + (l & 31), 2 * s + h));
-    const int kr0 = 16 * s + 8 * (q >> 1) + rr;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int nn = c0 + 32 * j + 16 * (q & 1) + 4 * c;
-        const i16x4 lo = lds_read_tr16(b + b_off(kr0, nn));
-        const i16x4 hi = lds_read_tr16(b + b_off(kr0 + 4, nn));
-        typedef short i16x8 __attribute__((ext_vector_type(8)));
-        const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        f.b[j] = __builtin_bit_cast(bf16x8, v);
-    }
-}
-
 // acc[i][j] += B-fragment j x A-fragment i for the first NB row blocks
 template <int MI, int NJ, int NB>
 __device__ inline void mma(const Frags<MI, NJ>& f, f32x16 (&acc)[MI][NJ]) {
@@ -107,11 +87,15 @@ __device__ inline void mma(const Frags<MI, NJ>& f, f32x16 (&acc)[MI][NJ]) {
 
 // fragment read number R of k step s, in the order the MFMAs (column block major) first
 // need them: B block 0, A blocks 0 .. NB - 1, then B blocks 1 .. NJ - 1
-template <int MI, int NJ, int NB, int R>
+template <int MI, int NJ, int NB, int R, bool B_NK>
 __device__ inline void read_one(Frags<MI, NJ>& f, const uint16_t* a, const uint16_t* b, int s, int r0, int c0) {
     const int l = threadIdx.x & 63, h = l >> 5;
     if constexpr (R >= 1 && R <= NB) {
         f.a[R - 1] = *(const bf16x8*)(a + a_off(r0 + 32 * (R - 1) + (l & 31), 2 * s + h));
+    } else if constexpr (B_NK) {
+        // k-contiguous weights: the slice is [256 n][32 k] in the A layout
+        constexpr int j = R == 0 ? 0 : R - NB;
+        f.b[j] = *(const bf16x8*)(b + a_off(c0 + 32 * j + (l & 31), 2 * s + h));
     } else {
         constexpr int j = R == 0 ? 0 : R - NB;
         const int q = l >> 4, rr = (l >> 2) & 3, c = l & 3;
@@ -126,7 +110,7 @@ __device__ inline void read_one(Frags<MI, NJ>& f, const uint16_t* a, const uint1
 }
 
 
-template <int BM, int WAVES_M, int STAGES, typename OutT>
+template <int BM, int WAVES_M, int STAGES, bool B_NK, typename OutT>
 __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
     typedef Cfg<BM, WAVES_M, STAGES> C;
     constexpr int MI = C::MI, NJ = C::NJ;
@@ -214,6 +198,13 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
                 const bool ok = live && kk + 8 * a_chunk < p.k;
                 const uint32_t wpart = (uint32_t)(16 * (C::A_LOADS * wave_u + d)) * k2 + (uint32_t)kk * 2u;
                 load_lds16(ra, lds_a + (uint32_t)slot * (C::ASLICE * 2) + d * 1024u, ok ? a_lane + wpart : kOOB);
+            } else if constexpr (B_NK) {
+                // [n][k] weights: row col0 + 16 (4 wave + u) + l / 4, chunk a_chunk (the A roles);
+                // rows past n fall outside the descriptor
+                constexpr int u = d - C::A_LOADS;
+                const bool ok = live && kk + 8 * a_chunk < p.k;
+                const uint32_t wpart = (uint32_t)(col0 + 16 * (4 * wave_u + u)) * k2 + (uint32_t)kk * 2u;
+                load_lds16(rb, lds_b + (uint32_t)slot * (BSLICE * 2) + u * 1024u, ok ? a_lane + wpart : kOOB);
             } else {
                 // k row kk + 2 (4 wave + u) + l / 32, columns col0 + b_ch8 .. + 7
                 constexpr int u = d - C::A_LOADS;
@@ -247,7 +238,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
                 }
                 if constexpr (o < ND) dma_one(o_c, stage);
-                if constexpr (o < NR) read_one<MI, NJ, NB, o>(nxt, a, b, s, r0w, c0w);
+                if constexpr (o < NR) read_one<MI, NJ, NB, o, B_NK>(nxt, a, b, s, r0w, c0w);
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
@@ -260,7 +251,8 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
             // the previous tile still in flight only raise the count, so this can only wait longer.
             wait_vm<C::PER * (STAGES - 2)>();
             lds_barrier();
-            if constexpr (NB > 0) read_frags<MI, NJ, NB>(f0, sm.ring.a[0], sm.ring.b[0], 0, r0w, c0w);
+            if constexpr (NB > 0)
+                static_for<0, NB + NJ>([&](auto r_c) { read_one<MI, NJ, NB, decltype(r_c)::value, B_NK>(f0, sm.ring.a[0], sm.ring.b[0], 0, r0w, c0w); });
             for (int kt = 0; kt + 1 < nk; ++kt) {
                 const int slot = kt % STAGES, ns = (kt + 1) % STAGES;
                 phase(nb_c, std::true_type{}, f0, f1, sm.ring.a[slot], sm.ring.b[slot], 1, kt + STAGES - 1);
@@ -303,8 +295,13 @@ bool ragged_m_bf16_fast_ok(const MParams& p) {
 }
 
 hipError_t launch_ragged_m_bf16_fast(const MParams& p, int grid, hipStream_t s) {
-    if (p.out_f32) hipLaunchKernelGGL((mb::kernel<GG_TILE, float>), dim3(grid), dim3(mb::NT), 0, s, p);
-    else hipLaunchKernelGGL((mb::kernel<GG_TILE, uint16_t>), dim3(grid), dim3(mb::NT), 0, s, p);
+    if (p.rhs_nk) {
+        if (p.out_f32) hipLaunchKernelGGL((mb::kernel<GG_TILE, true, float>), dim3(grid), dim3(mb::NT), 0, s, p);
+        else hipLaunchKernelGGL((mb::kernel<GG_TILE, true, uint16_t>), dim3(grid), dim3(mb::NT), 0, s, p);
+    } else {
+        if (p.out_f32) hipLaunchKernelGGL((mb::kernel<GG_TILE, false, float>), dim3(grid), dim3(mb::NT), 0, s, p);
+        else hipLaunchKernelGGL((mb::kernel<GG_TILE, false, uint16_t>), dim3(grid), dim3(mb::NT), 0, s, p);
+    }
     return hipGetLastError();
 }
 

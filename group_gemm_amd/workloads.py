@@ -58,11 +58,16 @@ WORKLOADS = {
         # correctness-only variant of the skewed workload with exactly-empty experts
         Workload(6, "deepseekv3_routed_bf16_zeros", "m", "bf16", "bf16", 32768, 7168, 2048,
                  256, "rank_zipf_gumbel_zeros", tokens=4096, top_k=8),
+        # data gradient of the Mixtral-like up-projection (Table 7 class dgrad_wi): the
+        # output gradient [8192, 14336] times each expert's stored weights [4096, 14336]^T
+        Workload(7, "mixtral8x7b_dgrad_bf16", "m_nk", "bf16", "bf16", 8192, 14336, 4096, 8,
+                 "topk_normal_logits", tokens=4096, top_k=2),
     ]
 }
 
-# the routing stream of the MXFP8 workload is the bf16 one's, so both see the same sizes
-_ROUTING_WID = {4: 2}
+# the MXFP8 and data-gradient workloads reuse the bf16 forward one's routing stream, so all
+# three see the same sizes
+_ROUTING_WID = {4: 2, 7: 2}
 
 
 def rng(wid: int, stream: int, seed: int = 0) -> np.random.Generator:
@@ -174,7 +179,8 @@ def make_inputs(w: Workload, device="cpu", seed: int = 0, gs: np.ndarray | None 
     """Operands of a workload as torch tensors on ``device``.
 
     Returns a dict with ``group_sizes`` (int32), and for op "m": ``lhs`` [m,k], ``rhs``
-    [g,k,n]; for op "k": ``lhs`` [m,k], ``dout`` [m,n].  bf16 operands are torch.bfloat16;
+    [g,k,n]; for op "m_nk": ``lhs`` [m,k], ``rhs`` [g,n,k] (k contiguous); for op "k":
+    ``lhs`` [m,k], ``dout`` [m,n].  bf16 operands are torch.bfloat16;
     MXFP8 operands are uint8 e4m3 codes plus ``lhs_scale`` [m,k/32] and ``rhs_scale``
     [g,k/32,n] (uint8 E8M0)."""
     if gs is None:
@@ -187,6 +193,12 @@ def make_inputs(w: Workload, device="cpu", seed: int = 0, gs: np.ndarray | None 
     elif w.op == "k":
         out["lhs"] = _randn((m, k), w.wid, 1, seed, device).to(torch.bfloat16)
         out["dout"] = _randn((m, n), w.wid, 2, seed, device).to(torch.bfloat16)
+    elif w.op == "m_nk":
+        out["lhs"] = _randn((m, k), w.wid, 1, seed, device).to(torch.bfloat16)
+        rhs = torch.empty((g, n, k), device=device, dtype=torch.bfloat16)
+        for h in range(g):
+            rhs[h] = _randn((n, k), w.wid, 2, seed * 65536 + h, device, std=1 / math.sqrt(k)).to(torch.bfloat16)
+        out["rhs"] = rhs
     elif w.in_dtype == "bf16":
         out["lhs"] = _randn((m, k), w.wid, 1, seed, device).to(torch.bfloat16)
         rhs = torch.empty((g, k, n), device=device, dtype=torch.bfloat16)

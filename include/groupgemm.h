@@ -40,14 +40,14 @@
 extern "C" {
 #endif
 
-#define GG_ABI_VERSION 1
+#define GG_ABI_VERSION 2
 
 typedef enum {
     GG_OK = 0,
     GG_ERR_NULL_PTR = 1,           /* a required pointer is NULL                          */
     GG_ERR_BAD_SHAPE = 2,          /* negative m/k/n, g < 1, g above GG_MAX_GROUPS, ...    */
     GG_ERR_BAD_DTYPE = 3,          /* unsupported in/out element type combination          */
-    GG_ERR_MISALIGNED = 4,         /* a pointer is not 4-byte aligned                       */
+    GG_ERR_MISALIGNED = 4,         /* a pointer is not aligned to its element (16 B for e4m3) */
     GG_ERR_WORKSPACE_TOO_SMALL = 5,
     GG_ERR_UNSUPPORTED = 6,        /* e.g. MXFP8 with k not a multiple of 32               */
     GG_ERR_HIP = 7                 /* a HIP runtime call failed (launch, device query)      */
@@ -94,6 +94,21 @@ gg_status ragged_dot_m(const void* lhs, const void* rhs, const int32_t* group_si
                        int64_t m, int64_t k, int64_t n, int32_t g, gg_dtype in_dtype,
                        gg_dtype out_dtype, const uint8_t* lhs_scale, const uint8_t* rhs_scale,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ragged_dot_m_nk -- ragged_dot_m with each group's matrix stored [n, k] (k contiguous):
+ * the data-gradient classes, which contract the weight's output-feature axis.
+ * ("Group-GEMM in XLA", Part 4 Table 7, classes dgrad_wi and dgrad_wo: rhs contracting
+ * dimension 2, so the weights are used as stored, with no transposed copy.)
+ *   out[r, :] = lhs[r, :] . rhs_nk[h]^T   for every row r of group h;   rows r >= sum(sizes) = 0.
+ *   lhs    [m, k]      bf16            e.g. dgrad_wi: the output gradient [M, N_fwd]
+ *   rhs_nk [g, n, k]   bf16            e.g. dgrad_wi: the forward weights [E, K_fwd, N_fwd]
+ *   out    [m, n]      bf16 or fp32    e.g. dgrad_wi: the input gradient [M, K_fwd]
+ * Requires 16-byte aligned lhs, rhs_nk and out and k % 8 == 0, n % 8 == 0; other element
+ * types or shapes return GG_ERR_UNSUPPORTED.  Workspace, status and errors as
+ * ragged_dot_m. */
+gg_status ragged_dot_m_nk(const void* lhs, const void* rhs_nk, const int32_t* group_sizes, void* out,
+                          int64_t m, int64_t k, int64_t n, int32_t g, gg_dtype in_dtype,
+                          gg_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ragged_dot_k -- contracting ragged dot, the weight-gradient case: the contracted
  * dimension m is ragged and the group index appears in the output.

@@ -89,6 +89,15 @@ def ragged_dot_m(lhs, rhs, group_sizes, lhs_scale=None, rhs_scale=None, rows=Non
     return out
 
 
+def ragged_dot_m_nk(lhs, rhs_nk, group_sizes, rows=None):
+    """fp64 result of the ragged dot whose weights are contracted on their last axis
+    ("Group-GEMM in XLA", Part 4 Table 7, classes dgrad_wi / dgrad_wo: rhs contracting
+    dimension 2): out[r, :] = lhs[r, :] . rhs_nk[h]^T for the rows r of group h, with
+    rhs_nk [g, n, k].  The same sum as ragged_dot_m over the transposed weights."""
+    rhs_nk = np.asarray(rhs_nk)
+    return ragged_dot_m(lhs, np.swapaxes(rhs_nk, 1, 2), group_sizes, rows=rows)
+
+
 def ragged_dot_k(lhs, dout, group_sizes, pairs=None):
     """fp64 result of the contracting ragged dot: [g, k, n], or the rows out[g_q, i_q, :]
     for the (g, i) pairs given as an int array of shape [npairs, 2]."""

@@ -22,7 +22,7 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for required in ("ragged_dot_m", "ragged_dot_k", "padded_dot", "gg_workspace_bytes", "gg_schedule",
+    for required in ("ragged_dot_m", "ragged_dot_m_nk", "ragged_dot_k", "padded_dot", "gg_workspace_bytes", "gg_schedule",
                      "gg_read_device_status", "gg_status_string", "gg_abi_version"):
         assert required in names
 
@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert B.abi_version() == 1
+    assert B.abi_version() == 2
     for code in range(8):
         assert B.status_string(code)
 
@@ -64,6 +64,21 @@ def test_ragged_m_host_validation():
     assert _m(wsb=WS_SMALL) == 5                 # GG_ERR_WORKSPACE_TOO_SMALL
     assert _m(ind=2, k=48, ls=P, rs=P) == 6      # e4m3 needs k % 32 == 0
     assert _m(ind=2, k=64, ls=NULL, rs=P) == 1   # e4m3 needs scales
+
+
+def test_ragged_m_nk_host_validation():
+    def nk(lhs=P, rhs=P, gs=P, out=P, m=64, k=64, n=64, g=4, ind=1, outd=1, ws=P, wsb=4096):
+        return B.lib().ragged_dot_m_nk(lhs, rhs, gs, out, m, k, n, g, ind, outd, ws, wsb, None)
+    assert nk(gs=NULL) == 1
+    assert nk(rhs=NULL) == 1
+    assert nk(g=0) == 2
+    assert nk(ind=0, outd=0) == 6                # fp32 [g,n,k] weights: not offered
+    assert nk(ind=2) == 6                        # nor e4m3
+    assert nk(outd=2) == 3                       # e4m3 output
+    assert nk(rhs=ctypes.c_void_p(0x10008)) == 4 # the ring path needs 16-byte alignment
+    assert nk(k=60) == 6                         # k % 8
+    assert nk(n=12) == 6                         # n % 8
+    assert nk(wsb=WS_SMALL) == 5
 
 
 def test_ragged_k_host_validation():

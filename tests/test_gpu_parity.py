@@ -194,6 +194,34 @@ def test_ragged_m_mxfp8_ring(case):
         assert np.linalg.norm(y32 - ref) <= 1e-4 * np.linalg.norm(ref), f"mx ring case {case}, fp32 out, normwise"
 
 
+# [g,n,k] weights (the dgrad classes): same cases shapes as the forward form, the oracle
+# fed the same values with the weights contracted on their last axis
+NK_CASES = [
+    (300, 256, 512, [100, 0, 150, 50]),
+    (513, 96, 136, [257, 256]),
+    (700, 264, 128, [1, 255, 256, 150, 0, 1]),   # k tail (264 = 8 slices + 8), sum < m
+    (1100, 1024, 1000, [0, 600, 7, 300, 193]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(NK_CASES)))
+def test_ragged_m_nk(case):
+    m, k, n, gs = NK_CASES[case]
+    say("ragged_m_nk", m, k, n, len(gs))
+    d = to_dev(W.small_inputs("m", "bf16", m, k, n, gs, seed=60 + case))
+    rhs_nk = d["rhs"].transpose(1, 2).contiguous()   # [g, n, k]
+    ref = oracle.ragged_dot_m_nk(raw(d["lhs"]), raw(rhs_nk), raw(d["group_sizes"]))
+    out = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    y = gg().ragged_dot_m(d["lhs"], rhs_nk, d["group_sizes"], out=out, rhs_layout="nk")
+    torch.cuda.synchronize()
+    check_bf16(y, ref, f"nk case {case}")
+    assert torch.all(y[sum(gs):] == 0)
+    if case == 0:
+        y32 = gg().ragged_dot_m(d["lhs"], rhs_nk, d["group_sizes"], out_dtype=torch.float32, rhs_layout="nk")
+        torch.cuda.synchronize()
+        check_fp32(y32, ref, "nk case 0, fp32 out")
+
+
 def test_device_status_and_clamping():
     say("invalid group sizes")
     m, k, n = 200, 64, 64

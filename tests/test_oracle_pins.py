@@ -203,6 +203,36 @@ def test_k_is_the_weight_gradient_of_m():
     assert math.isclose(lhs_side, rhs_side, rel_tol=1e-12, abs_tol=1e-12)
 
 
+@pytest.mark.parametrize("gs,m", [([0, 0, 0], 5), ([2, 0, 3], 5), ([1, 1, 1, 1], 6), ([0, 4, 0], 4)])
+def test_m_nk_brute_force(gs, m):
+    """rhs contracted on its last axis (Table 7, dgrad classes): triple loop over rhs[h, j, t]."""
+    k, n = 3, 5
+    r = np.random.default_rng(11)
+    lhs, rhs_nk = _f32(r.standard_normal((m, k))), _f32(r.standard_normal((len(gs), n, k)))
+    out = oracle.ragged_dot_m_nk(lhs, rhs_nk, gs)
+    expect = np.zeros((m, n))
+    row = 0
+    for h, s in enumerate(gs):
+        for _ in range(s):
+            for j in range(n):
+                expect[row, j] = sum(float(lhs[row, t]) * float(rhs_nk[h, j, t]) for t in range(k))
+            row += 1
+    np.testing.assert_allclose(out, expect, rtol=1e-14, atol=1e-14)
+
+
+def test_m_nk_is_the_data_gradient_of_m():
+    """<dY, ragged_dot_m(X, W)> = <ragged_dot_m_nk(dY, W), X> for any X, with W [g, K, N] as
+    stored: the dgrad class is the data gradient of the forward class it is paired with
+    (Table 7: fwd_wi [M,K] x [E,K,N] -> [M,N]; dgrad_wi [M,N] x [E,K,N] -> [M,K])."""
+    m, K, N, gs = 21, 5, 7, [6, 0, 9, 6]
+    r = np.random.default_rng(12)
+    X, dY = _f32(r.standard_normal((m, K))), _f32(r.standard_normal((m, N)))
+    Wt = _f32(r.standard_normal((len(gs), K, N)))
+    lhs_side = float(np.sum(dY.astype(np.float64) * oracle.ragged_dot_m(X, Wt, gs)))
+    rhs_side = float(np.sum(oracle.ragged_dot_m_nk(dY, Wt, gs) * X.astype(np.float64)))
+    assert math.isclose(lhs_side, rhs_side, rel_tol=1e-12, abs_tol=1e-12)
+
+
 def test_k_pairs_select_rows_of_the_full_result():
     m, k, n, gs = 14, 5, 3, [3, 0, 11]
     r = np.random.default_rng(11)

@@ -31,6 +31,7 @@ def test_workload_shapes_of_routing():
     assert (gs3 < 16).sum() >= 3 and (gs3 > 1000).sum() >= 3    # skewed: tiny and huge groups
     gz = W.group_sizes(W.WORKLOADS["deepseekv3_routed_bf16_zeros"])
     assert (gz == 0).sum() == 4
+    assert np.array_equal(gs2, W.group_sizes(W.WORKLOADS["mixtral8x7b_dgrad_bf16"]))
     gs5 = W.group_sizes(W.WORKLOADS["llama4scout_wgrad_bf16"])
     assert gs5.max() > 2 * gs5.mean()                           # Dirichlet(0.5) is uneven
 
