@@ -38,6 +38,11 @@ def lib():
         L.ragged_dot_m.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
         L.ragged_dot_k.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, ctypes.c_int, vp, sz, vp]
         L.ragged_dot_m_nk.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, ctypes.c_int, vp, sz, vp]
+        f32 = ctypes.c_float
+        L.ragged_dot_m_epilogue.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp,
+                                            i64, f32, f32, vp, sz, vp]
+        L.ragged_dot_k_epilogue.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, ctypes.c_int, f32, f32, vp,
+                                            sz, vp]
         L.padded_dot.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i32, i64, ctypes.c_int, ctypes.c_int,
                                  vp, vp, vp, sz, vp]
         L.gg_schedule.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
@@ -45,7 +50,8 @@ def lib():
         L.gg_status_string.argtypes = [ctypes.c_int]
         L.gg_status_string.restype = ctypes.c_char_p
         L.gg_abi_version.restype = ctypes.c_int
-        for f in ("ragged_dot_m", "ragged_dot_m_nk", "ragged_dot_k", "padded_dot", "gg_schedule", "gg_read_device_status"):
+        for f in ("ragged_dot_m", "ragged_dot_m_nk", "ragged_dot_m_epilogue", "ragged_dot_k", "ragged_dot_k_epilogue",
+                  "padded_dot", "gg_schedule", "gg_read_device_status"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -86,11 +92,13 @@ def _workspace(op, m, k, n, g, capacity, in_dtype, device, workspace):
 
 
 def ragged_dot_m(lhs, rhs, group_sizes, out=None, out_dtype=None, lhs_scale=None, rhs_scale=None, workspace=None,
-                 rhs_layout="kn"):
+                 rhs_layout="kn", bias=None, alpha=1.0, beta=0.0):
     """out[m,n]: row block of group h of lhs [m,k] times rhs[h] [k,n]; rows past
     sum(group_sizes) are 0.  e4m3 inputs (uint8 codes) need E8M0 lhs_scale [m,k/32] and
     rhs_scale [g,k/32,n].  rhs_layout="nk" takes rhs as [g,n,k] (k contiguous) and
-    multiplies by rhs[h]^T: the data-gradient classes, bf16 only (ragged_dot_m_nk)."""
+    multiplies by rhs[h]^T: the data-gradient classes, bf16 only (ragged_dot_m_nk).
+    bias (fp32 [g, >=n], unit column stride), alpha, beta: out = alpha * (lhs . rhs[h]) +
+    bias[h] + beta * out, in place (ragged_dot_m_epilogue; beta != 0 reads `out`)."""
     m, k = lhs.shape
     if rhs_layout == "nk":
         g, n, k2 = rhs.shape
@@ -105,6 +113,21 @@ def ragged_dot_m(lhs, rhs, group_sizes, out=None, out_dtype=None, lhs_scale=None
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=lhs.device)
     ws = _workspace("ragged_m", m, k, n, g, 0, lhs.dtype, lhs.device, workspace)
+    if bias is not None or alpha != 1.0 or beta != 0.0:
+        if rhs_layout != "kn":
+            raise ValueError("the epilogue takes [g,k,n] weights")
+        if beta != 0.0 and out is None:
+            raise ValueError("beta != 0 accumulates into `out`, which must be given")
+        stride = 0
+        if bias is not None:
+            if bias.dtype != torch.float32 or bias.dim() != 2 or bias.shape[0] != g or bias.shape[1] < n or bias.stride(1) != 1:
+                raise ValueError("bias must be float32 [g, >=n] with unit column stride")
+            stride = bias.stride(0)
+        code = lib().ragged_dot_m_epilogue(_p(lhs), _p(rhs), _p(group_sizes), _p(out), m, k, n, g, GG_DT[lhs.dtype],
+                                           GG_DT[out.dtype], _p(lhs_scale), _p(rhs_scale), _p(bias), stride,
+                                           float(alpha), float(beta), _p(ws), ws.numel(), _stream(lhs.device))
+        _check(code, "ragged_dot_m_epilogue")
+        return out
     if rhs_layout == "nk":
         if lhs_scale is not None or rhs_scale is not None:
             raise ValueError("rhs_layout='nk' takes no scales")
@@ -119,8 +142,10 @@ def ragged_dot_m(lhs, rhs, group_sizes, out=None, out_dtype=None, lhs_scale=None
     return out
 
 
-def ragged_dot_k(lhs, dout, group_sizes, out=None, out_dtype=torch.float32, workspace=None):
-    """out[g,k,n]: out[h] = lhs[rows of h]^T . dout[rows of h]; empty groups give 0."""
+def ragged_dot_k(lhs, dout, group_sizes, out=None, out_dtype=torch.float32, workspace=None, alpha=1.0, beta=0.0):
+    """out[g,k,n]: out[h] = lhs[rows of h]^T . dout[rows of h]; empty groups give 0.
+    alpha, beta: out[h] = alpha * (...) + beta * out[h], in place (ragged_dot_k_epilogue;
+    beta = 1 accumulates over micro-steps)."""
     m, k = lhs.shape
     m2, n = dout.shape
     g = group_sizes.shape[0]
@@ -129,6 +154,14 @@ def ragged_dot_k(lhs, dout, group_sizes, out=None, out_dtype=torch.float32, work
     if out is None:
         out = torch.empty((g, k, n), dtype=out_dtype, device=lhs.device)
     ws = _workspace("ragged_k", m, k, n, g, 0, lhs.dtype, lhs.device, workspace)
+    if alpha != 1.0 or beta != 0.0:
+        if beta != 0.0 and out is None:
+            raise ValueError("beta != 0 accumulates into `out`, which must be given")
+        code = lib().ragged_dot_k_epilogue(_p(lhs), _p(dout), _p(group_sizes), _p(out), m, k, n, g, GG_DT[lhs.dtype],
+                                           GG_DT[out.dtype], float(alpha), float(beta), _p(ws), ws.numel(),
+                                           _stream(lhs.device))
+        _check(code, "ragged_dot_k_epilogue")
+        return out
     code = lib().ragged_dot_k(_p(lhs), _p(dout), _p(group_sizes), _p(out), m, k, n, g, GG_DT[lhs.dtype],
                               GG_DT[out.dtype], _p(ws), ws.numel(), _stream(lhs.device))
     _check(code, "ragged_dot_k")

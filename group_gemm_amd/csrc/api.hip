@@ -55,9 +55,18 @@ gg_status check_common(int64_t m, int64_t k, int64_t n, int32_t g, const int32_t
 }
 
 // ragged_dot_m body, shared with the batched stage of padded_dot (uniform_rows > 0).
+// Epilogue of the ring kernels: out = alpha * acc + bias[h] + beta * out.  `on` false: plain
+// store (every kernel family); true: only the ring kernels implement it.
+struct EpiArgs {
+    bool on = false;
+    const float* bias = nullptr;
+    int64_t bias_stride = 0;
+    float alpha = 1.f, beta = 0.f;
+};
+
 gg_status run_m(const void* lhs, const void* rhs, const int32_t* gs, void* out, int64_t m, int64_t k, int64_t n,
                 int32_t g, gg_dtype in, gg_dtype outd, const uint8_t* ls, const uint8_t* rs, uint32_t* status,
-                int uniform_rows, hipStream_t s, bool rhs_nk = false) {
+                int uniform_rows, hipStream_t s, bool rhs_nk = false, const EpiArgs& ep = EpiArgs()) {
     int cus;
     if (device_cus(&cus) != 0) return GG_ERR_HIP;
     gg::MParams p{};
@@ -65,6 +74,7 @@ gg_status run_m(const void* lhs, const void* rhs, const int32_t* gs, void* out, 
     p.m = (int)m; p.k = (int)k; p.n = (int)n; p.g = g; p.uniform_rows = uniform_rows;
     p.out_f32 = outd == GG_DT_F32;
     p.rhs_nk = rhs_nk ? 1 : 0;
+    p.epi = ep.on ? 1 : 0; p.bias = ep.bias; p.bias_stride = ep.bias_stride; p.alpha = ep.alpha; p.beta = ep.beta;
     hipError_t e;
     if (rhs_nk) {   // [g,n,k] weights: the bf16 ring kernel only
         const bool vec = aligned(lhs, 16) && aligned(rhs, 16) && aligned(out, 16) && k % 8 == 0 && n % 8 == 0;
@@ -73,6 +83,7 @@ gg_status run_m(const void* lhs, const void* rhs, const int32_t* gs, void* out, 
         if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
         e = gg::launch_ragged_m_bf16_fast(p, persistent_grid(bound, 1, cus), s);
     } else if (in == GG_DT_F32) {
+        if (ep.on) return GG_ERR_UNSUPPORTED;
         gg::TileShape ts = gg::tiles_m_f32();
         int64_t bound = (cdiv64(m, ts.bm) + g + 1) * cdiv64(n, ts.bn);
         if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
@@ -84,6 +95,7 @@ gg_status run_m(const void* lhs, const void* rhs, const int32_t* gs, void* out, 
         if (fast) ts = {gg::ragged_m_bf16_fast_bm(p), 256};
         int64_t bound = (cdiv64(m, ts.bm) + g + 1) * cdiv64(n, ts.bn);
         if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
+        if (ep.on && !fast) return GG_ERR_UNSUPPORTED;
         if (fast) e = gg::launch_ragged_m_bf16_fast(p, persistent_grid(bound, 1, cus), s);
         else e = gg::launch_ragged_m_bf16(p, persistent_grid(bound, 1, cus), vec, s);
     } else {
@@ -93,6 +105,7 @@ gg_status run_m(const void* lhs, const void* rhs, const int32_t* gs, void* out, 
         if (fast) ts = {256, 256};
         int64_t bound = (cdiv64(m, ts.bm) + g + 1) * cdiv64(n, ts.bn);
         if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
+        if (ep.on && !fast) return GG_ERR_UNSUPPORTED;
         if (fast) e = gg::launch_ragged_m_mx_fast(p, persistent_grid(bound, 1, cus), s);
         else e = gg::launch_ragged_m_e4m3(p, persistent_grid(bound, 1, cus), s);
     }
@@ -100,15 +113,18 @@ gg_status run_m(const void* lhs, const void* rhs, const int32_t* gs, void* out, 
 }
 
 gg_status run_k(const void* lhs, const void* dout, const int32_t* gs, void* out, int64_t m, int64_t k, int64_t n,
-                int32_t g, gg_dtype in, gg_dtype outd, uint32_t* status, int uniform_rows, hipStream_t s) {
+                int32_t g, gg_dtype in, gg_dtype outd, uint32_t* status, int uniform_rows, hipStream_t s,
+                const EpiArgs& ep = EpiArgs()) {
     int cus;
     if (device_cus(&cus) != 0) return GG_ERR_HIP;
     gg::KParams p{};
     p.lhs = lhs; p.dout = dout; p.group_sizes = gs; p.out = out; p.status = status;
     p.m = (int)m; p.k = (int)k; p.n = (int)n; p.g = g; p.uniform_rows = uniform_rows;
     p.out_f32 = outd == GG_DT_F32;
+    p.epi = ep.on ? 1 : 0; p.alpha = ep.alpha; p.beta = ep.beta;
     hipError_t e;
     if (in == GG_DT_F32) {
+        if (ep.on) return GG_ERR_UNSUPPORTED;
         gg::TileShape ts = gg::tiles_k_f32();
         int64_t bound = (int64_t)g * cdiv64(k, ts.bm) * cdiv64(n, ts.bn);
         if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
@@ -118,8 +134,9 @@ gg_status run_k(const void* lhs, const void* dout, const int32_t* gs, void* out,
         int64_t bound = (int64_t)g * cdiv64(k, ts.bm) * cdiv64(n, ts.bn);
         if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
         const bool vec = aligned(lhs, 16) && aligned(dout, 16) && k % 8 == 0 && n % 8 == 0;
-        if (vec && aligned(out, 16) && gg::ragged_k_bf16_fast_ok(p))
-            e = gg::launch_ragged_k_bf16_fast(p, persistent_grid(bound, 1, cus), s);
+        const bool fast = vec && aligned(out, 16) && gg::ragged_k_bf16_fast_ok(p);
+        if (ep.on && !fast) return GG_ERR_UNSUPPORTED;
+        if (fast) e = gg::launch_ragged_k_bf16_fast(p, persistent_grid(bound, 1, cus), s);
         else e = gg::launch_ragged_k_bf16(p, persistent_grid(bound, 1, cus), vec, s);
     }
     return e == hipSuccess ? GG_OK : GG_ERR_HIP;
@@ -210,6 +227,45 @@ gg_status ragged_dot_m_nk(const void* lhs, const void* rhs_nk, const int32_t* gr
     if (k % 8 != 0 || n % 8 != 0) return GG_ERR_UNSUPPORTED;
     return run_m(lhs, rhs_nk, group_sizes, out, m, k, n, g, in_dtype, out_dtype, nullptr, nullptr, (uint32_t*)workspace,
                  0, (hipStream_t)stream, true);
+}
+
+gg_status ragged_dot_m_epilogue(const void* lhs, const void* rhs, const int32_t* group_sizes, void* out, int64_t m,
+                                int64_t k, int64_t n, int32_t g, gg_dtype in_dtype, gg_dtype out_dtype,
+                                const uint8_t* lhs_scale, const uint8_t* rhs_scale, const float* bias, int64_t bias_stride,
+                                float alpha, float beta, void* workspace, size_t workspace_bytes, void* stream) {
+    if (bias && (bias_stride < n || !aligned(bias, 4))) return bias_stride < n ? GG_ERR_BAD_SHAPE : GG_ERR_MISALIGNED;
+    EpiArgs ep;
+    ep.on = bias != nullptr || alpha != 1.f || beta != 0.f;
+    ep.bias = bias; ep.bias_stride = bias_stride; ep.alpha = alpha; ep.beta = beta;
+    gg_status st = check_common(m, k, n, g, group_sizes, workspace, workspace_bytes, kHeader);
+    if (st != GG_OK) return st;
+    if (!m_dtypes_ok(in_dtype, out_dtype)) return GG_ERR_BAD_DTYPE;
+    if ((m * k > 0 && !lhs) || (k * n > 0 && !rhs) || (m * n > 0 && !out)) return GG_ERR_NULL_PTR;
+    const size_t es = elem_bytes(in_dtype);
+    if (!aligned(lhs, es) || !aligned(rhs, es) || !aligned(out, elem_bytes(out_dtype))) return GG_ERR_MISALIGNED;
+    if (in_dtype == GG_DT_E4M3) {
+        if (k % 32 != 0) return GG_ERR_UNSUPPORTED;
+        if ((m * k > 0 && !lhs_scale) || (k * n > 0 && !rhs_scale)) return GG_ERR_NULL_PTR;
+        if (!aligned(lhs, 16) || !aligned(rhs, 16)) return GG_ERR_MISALIGNED;
+    }
+    return run_m(lhs, rhs, group_sizes, out, m, k, n, g, in_dtype, out_dtype, lhs_scale, rhs_scale, (uint32_t*)workspace,
+                 0, (hipStream_t)stream, false, ep);
+}
+
+gg_status ragged_dot_k_epilogue(const void* lhs, const void* dout, const int32_t* group_sizes, void* out, int64_t m,
+                                int64_t k, int64_t n, int32_t g, gg_dtype in_dtype, gg_dtype out_dtype, float alpha,
+                                float beta, void* workspace, size_t workspace_bytes, void* stream) {
+    EpiArgs ep;
+    ep.on = alpha != 1.f || beta != 0.f;
+    ep.alpha = alpha; ep.beta = beta;
+    gg_status st = check_common(m, k, n, g, group_sizes, workspace, workspace_bytes, kHeader);
+    if (st != GG_OK) return st;
+    if (!k_dtypes_ok(in_dtype, out_dtype)) return GG_ERR_BAD_DTYPE;
+    if ((m * k > 0 && !lhs) || (m * n > 0 && !dout) || (k * n > 0 && !out)) return GG_ERR_NULL_PTR;
+    const size_t es = elem_bytes(in_dtype);
+    if (!aligned(lhs, es) || !aligned(dout, es) || !aligned(out, elem_bytes(out_dtype))) return GG_ERR_MISALIGNED;
+    return run_k(lhs, dout, group_sizes, out, m, k, n, g, in_dtype, out_dtype, (uint32_t*)workspace, 0,
+                 (hipStream_t)stream, ep);
 }
 
 gg_status ragged_dot_k(const void* lhs, const void* dout, const int32_t* group_sizes, void* out, int64_t m, int64_t k,

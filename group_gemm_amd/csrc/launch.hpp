@@ -21,6 +21,11 @@ struct MParams {
     int uniform_rows;           // > 0: every group has exactly this many rows (batched form)
     int out_f32;                // 1: fp32 output, 0: bf16 output
     int rhs_nk;                 // 1: rhs is [g,n,k] (k contiguous; the dgrad classes), 0: [g,k,n]
+    // epilogue (epi != 0): out = alpha * acc + bias[h, :] + beta * out, in place
+    int epi;
+    const float* bias;          // [g, bias_stride] fp32 rows, or NULL
+    int64_t bias_stride;
+    float alpha, beta;
 };
 
 // Contracting ragged dot: out[g,k,n] = per-group lhs[rows,k]^T . dout[rows,n].
@@ -33,6 +38,9 @@ struct KParams {
     int m, k, n, g;
     int uniform_rows;
     int out_f32;
+    // epilogue (epi != 0): out[h] = alpha * acc + beta * out[h], in place
+    int epi;
+    float alpha, beta;
 };
 
 // Kernel families.  Each launcher returns the hipError_t of its launch.

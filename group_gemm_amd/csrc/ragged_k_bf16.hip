@@ -71,7 +71,7 @@ __device__ inline void read_one(Frags& f, const uint16_t* a, const uint16_t* b, 
     else f.b[R == 0 ? 0 : R - NB] = frag(b, s, c0w, R == 0 ? 0 : R - NB);
 }
 
-template <typename OutT>
+template <bool EPI, typename OutT>
 __global__ __launch_bounds__(NT, 1) void kernel(KParams p) {
     __shared__ Smem sm;
     const int t = threadIdx.x, l = t & 63, wave = t >> 6;
@@ -208,12 +208,18 @@ __global__ __launch_bounds__(NT, 1) void kernel(KParams p) {
             });
         };
         if (nk > 0) with_nb<MI>(nb, run);
-        lds_barrier();   // every wave is done with the ring before it is reused
+        // Every ring load has landed (the zero-fill loads of slices past the end may still be
+        // in flight, and the epilogue strips overlap their slots) and every wave is done
+        // reading the ring before it is reused.
+        wait_vm<0>();
+        lds_barrier();
 
         const rsrc_t ro = make_rsrc((const char*)p.out + ((size_t)grp * p.k + i0) * p.n * osz, (uint32_t)(rows_valid * p.n * osz));
         static_assert(4 * 32 * (WCOLS + 4) * 4 <= (int)sizeof(sm.ring), "epilogue strips fit the ring");
-        store_acc<MI, NJ, WCOLS, OutT>(acc, reinterpret_cast<float*>(&sm.ring) + wave * 32 * (WCOLS + 4), ro, p.n, j0, r0w, c0w);
-        if constexpr (osz == 2) lds_barrier();   // strips read before the next tile's ring loads land there
+        const EpiTile ep{nullptr, p.alpha, p.beta};
+        store_acc<MI, NJ, WCOLS, OutT, EPI>(acc, reinterpret_cast<float*>(&sm.ring) + wave * 32 * (WCOLS + 4), ro, p.n, j0, r0w,
+                                            c0w, ep);
+        if constexpr (osz == 2 || EPI) lds_barrier();   // strips read before the next tile's ring loads land there
     }
     wait_vm<0>();   // no ring load may still be writing LDS when the workgroup ends
 }
@@ -230,8 +236,13 @@ bool ragged_k_bf16_fast_ok(const KParams& p) {
 }
 
 hipError_t launch_ragged_k_bf16_fast(const KParams& p, int grid, hipStream_t s) {
-    if (p.out_f32) hipLaunchKernelGGL((kr::kernel<float>), dim3(grid), dim3(kr::NT), 0, s, p);
-    else hipLaunchKernelGGL((kr::kernel<uint16_t>), dim3(grid), dim3(kr::NT), 0, s, p);
+    if (p.epi) {
+        if (p.out_f32) hipLaunchKernelGGL((kr::kernel<true, float>), dim3(grid), dim3(kr::NT), 0, s, p);
+        else hipLaunchKernelGGL((kr::kernel<true, uint16_t>), dim3(grid), dim3(kr::NT), 0, s, p);
+    } else {
+        if (p.out_f32) hipLaunchKernelGGL((kr::kernel<false, float>), dim3(grid), dim3(kr::NT), 0, s, p);
+        else hipLaunchKernelGGL((kr::kernel<false, uint16_t>), dim3(grid), dim3(kr::NT), 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -110,7 +110,7 @@ __device__ inline void read_one(Frags<MI, NJ>& f, const uint16_t* a, const uint1
 }
 
 
-template <int BM, int WAVES_M, int STAGES, bool B_NK, typename OutT>
+template <int BM, int WAVES_M, int STAGES, bool B_NK, bool EPI, typename OutT>
 __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
     typedef Cfg<BM, WAVES_M, STAGES> C;
     constexpr int MI = C::MI, NJ = C::NJ;
@@ -265,12 +265,18 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
             mma<MI, NJ, NB>(f1, acc);
         };
         if (nk > 0) with_nb<MI>(nb, run);
-        lds_barrier();   // every wave is done with the ring before it is reused
+        // Every ring load has landed (the zero-fill loads of slices past the end may still be
+        // in flight, and the epilogue strips overlap their slots) and every wave is done
+        // reading the ring before it is reused.
+        wait_vm<0>();
+        lds_barrier();
 
         const rsrc_t ro = make_rsrc((const char*)p.out + (size_t)row0 * p.n * osz, (uint32_t)(rows_valid * p.n * osz));
         static_assert(4 * 32 * (C::WCOLS + 4) * 4 <= (int)sizeof(sm.ring), "epilogue strips fit the ring");
-        store_acc<MI, NJ, C::WCOLS, OutT>(acc, reinterpret_cast<float*>(&sm.ring) + wave * 32 * (C::WCOLS + 4), ro, p.n, col0, r0w, c0w);
-        if constexpr (osz == 2) lds_barrier();   // strips read before the next tile's ring loads land there
+        const EpiTile ep{p.bias ? p.bias + (size_t)grp * p.bias_stride : nullptr, p.alpha, p.beta};
+        store_acc<MI, NJ, C::WCOLS, OutT, EPI>(acc, reinterpret_cast<float*>(&sm.ring) + wave * 32 * (C::WCOLS + 4), ro, p.n,
+                                               col0, r0w, c0w, ep);
+        if constexpr (osz == 2 || EPI) lds_barrier();   // strips read before the next tile's ring loads land there
     }
     wait_vm<0>();   // no ring load may still be writing LDS when the workgroup ends
 }
@@ -294,13 +300,19 @@ bool ragged_m_bf16_fast_ok(const MParams& p) {
     return p.k % 8 == 0 && p.n % 8 == 0 && w < (1ull << 31) && a < (1ull << 31) && o < (1ull << 31);
 }
 
+template <bool B_NK, bool EPI>
+static void launch_mb(const MParams& p, int grid, hipStream_t s) {
+    if (p.out_f32) hipLaunchKernelGGL((mb::kernel<GG_TILE, B_NK, EPI, float>), dim3(grid), dim3(mb::NT), 0, s, p);
+    else hipLaunchKernelGGL((mb::kernel<GG_TILE, B_NK, EPI, uint16_t>), dim3(grid), dim3(mb::NT), 0, s, p);
+}
+
 hipError_t launch_ragged_m_bf16_fast(const MParams& p, int grid, hipStream_t s) {
     if (p.rhs_nk) {
-        if (p.out_f32) hipLaunchKernelGGL((mb::kernel<GG_TILE, true, float>), dim3(grid), dim3(mb::NT), 0, s, p);
-        else hipLaunchKernelGGL((mb::kernel<GG_TILE, true, uint16_t>), dim3(grid), dim3(mb::NT), 0, s, p);
+        if (p.epi) launch_mb<true, true>(p, grid, s);
+        else launch_mb<true, false>(p, grid, s);
     } else {
-        if (p.out_f32) hipLaunchKernelGGL((mb::kernel<GG_TILE, false, float>), dim3(grid), dim3(mb::NT), 0, s, p);
-        else hipLaunchKernelGGL((mb::kernel<GG_TILE, false, uint16_t>), dim3(grid), dim3(mb::NT), 0, s, p);
+        if (p.epi) launch_mb<false, true>(p, grid, s);
+        else launch_mb<false, false>(p, grid, s);
     }
     return hipGetLastError();
 }

@@ -87,7 +87,7 @@ __device__ inline void read_b(Frags& f, int j, const Slot& s, int c0w, int cp) {
     f.sb[j] = s.bs[cp * 2 * BN + h * BN + c0w + 32 * j + (l & 31)];   // E8M0 of (column, k block 2 ks + h)
 }
 
-template <typename OutT>
+template <bool EPI, typename OutT>
 __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
     __shared__ Smem sm;
     const int t = threadIdx.x, l = t & 63, wave = t >> 6;
@@ -258,12 +258,18 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
             phase2(std::false_type{}, sm.ring[0], 0);
         };
         if (nk > 0) with_nb<MI>(nb, run);
-        lds_barrier();   // every wave is done with the ring before it is reused
+        // Every ring load has landed (the zero-fill loads of slices past the end may still be
+        // in flight, and the epilogue strips overlap their slots) and every wave is done
+        // reading the ring before it is reused.
+        wait_vm<0>();
+        lds_barrier();
 
         const rsrc_t ro = make_rsrc((const char*)p.out + (size_t)row0 * p.n * osz, (uint32_t)(rows_valid * p.n * osz));
         static_assert(4 * 32 * (WCOLS + 4) * 4 <= (int)sizeof(sm.ring), "epilogue strips fit the ring");
-        store_acc<MI, NJ, WCOLS, OutT>(acc, reinterpret_cast<float*>(&sm.ring[0]) + wave * 32 * (WCOLS + 4), ro, p.n, col0, r0w, c0w);
-        if constexpr (osz == 2) lds_barrier();   // strips read before the next tile's ring loads land there
+        const EpiTile ep{p.bias ? p.bias + (size_t)grp * p.bias_stride : nullptr, p.alpha, p.beta};
+        store_acc<MI, NJ, WCOLS, OutT, EPI>(acc, reinterpret_cast<float*>(&sm.ring[0]) + wave * 32 * (WCOLS + 4), ro, p.n, col0,
+                                            r0w, c0w, ep);
+        if constexpr (osz == 2 || EPI) lds_barrier();   // strips read before the next tile's ring loads land there
     }
     wait_vm<0>();   // no ring load may still be writing LDS when the workgroup ends
 }
@@ -279,8 +285,13 @@ bool ragged_m_mx_fast_ok(const MParams& p) {
 }
 
 hipError_t launch_ragged_m_mx_fast(const MParams& p, int grid, hipStream_t s) {
-    if (p.out_f32) hipLaunchKernelGGL((mx::kernel<float>), dim3(grid), dim3(mx::NT), 0, s, p);
-    else hipLaunchKernelGGL((mx::kernel<uint16_t>), dim3(grid), dim3(mx::NT), 0, s, p);
+    if (p.epi) {
+        if (p.out_f32) hipLaunchKernelGGL((mx::kernel<true, float>), dim3(grid), dim3(mx::NT), 0, s, p);
+        else hipLaunchKernelGGL((mx::kernel<true, uint16_t>), dim3(grid), dim3(mx::NT), 0, s, p);
+    } else {
+        if (p.out_f32) hipLaunchKernelGGL((mx::kernel<false, float>), dim3(grid), dim3(mx::NT), 0, s, p);
+        else hipLaunchKernelGGL((mx::kernel<false, uint16_t>), dim3(grid), dim3(mx::NT), 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define GG_ABI_VERSION 2
+#define GG_ABI_VERSION 3
 
 typedef enum {
     GG_OK = 0,
@@ -109,6 +109,34 @@ gg_status ragged_dot_m(const void* lhs, const void* rhs, const int32_t* group_si
 gg_status ragged_dot_m_nk(const void* lhs, const void* rhs_nk, const int32_t* group_sizes, void* out,
                           int64_t m, int64_t k, int64_t n, int32_t g, gg_dtype in_dtype,
                           gg_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ragged_dot_m_epilogue -- ragged_dot_m with a fused epilogue, in place on out:
+ *   out[r, :] = alpha * (lhs[r, :] . rhs[h]) + bias[h, :] + beta * out[r, :]
+ * for every row r of group h; rows r >= sum(sizes) are 0 as in ragged_dot_m.
+ * ("Group-GEMM in XLA", Part 2: the grouped-GEMM configuration carries alpha and beta;
+ * "[Triton/Gluon] Merge MoE MXFP8 GEMM into existing _moe_gemm_a8w8 kernel", review: a
+ * per-expert bias [E, N] indexed with its real row stride.)
+ *   bias [g, bias_stride] fp32 (bias_stride >= n, 4-byte aligned), or NULL for none.
+ *   beta != 0 reads out (bf16 or fp32, as written by a previous call) before writing it.
+ * Other arguments as ragged_dot_m.  A non-trivial epilogue (bias, alpha != 1 or beta != 0)
+ * runs on the vectorised bf16 / MXFP8 paths (16-byte aligned operands and output; k, n % 8
+ * for bf16; k % 128, n % 16 for e4m3) and returns GG_ERR_UNSUPPORTED elsewhere. */
+gg_status ragged_dot_m_epilogue(const void* lhs, const void* rhs, const int32_t* group_sizes, void* out,
+                                int64_t m, int64_t k, int64_t n, int32_t g, gg_dtype in_dtype,
+                                gg_dtype out_dtype, const uint8_t* lhs_scale, const uint8_t* rhs_scale,
+                                const float* bias, int64_t bias_stride, float alpha, float beta,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ragged_dot_k_epilogue -- ragged_dot_k with out[h] = alpha * (lhs_h^T . dout_h) + beta * out[h],
+ * in place: beta = 1 accumulates weight gradients over gradient-accumulation micro-steps
+ * ("Group-GEMM in XLA", Part 4 Tables 4/5: the models train with grad-accum up to 16).
+ * An empty group gives beta * out[h].  Other arguments as ragged_dot_k; a non-trivial
+ * epilogue runs on the vectorised bf16 path (16-byte aligned, k, n % 8) and returns
+ * GG_ERR_UNSUPPORTED elsewhere. */
+gg_status ragged_dot_k_epilogue(const void* lhs, const void* dout, const int32_t* group_sizes, void* out,
+                                int64_t m, int64_t k, int64_t n, int32_t g, gg_dtype in_dtype,
+                                gg_dtype out_dtype, float alpha, float beta, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* ragged_dot_k -- contracting ragged dot, the weight-gradient case: the contracted
  * dimension m is ragged and the group index appears in the output.

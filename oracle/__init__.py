@@ -98,6 +98,36 @@ def ragged_dot_m_nk(lhs, rhs_nk, group_sizes, rows=None):
     return ragged_dot_m(lhs, np.swapaxes(rhs_nk, 1, 2), group_sizes, rows=rows)
 
 
+def ragged_dot_m_epilogue(lhs, rhs, group_sizes, bias=None, alpha=1.0, beta=0.0, c=None, lhs_scale=None,
+                          rhs_scale=None):
+    """fp64 out[r, :] = alpha * (lhs[r, :] . rhs[h]) + bias[h, :n] + beta * c[r, :] for the rows r
+    of group h (the grouped-GEMM alpha / beta of "Group-GEMM in XLA" Part 2 and the
+    per-expert bias of the aiter MXFP8 MoE GEMM); rows past the groups' total are 0.
+    bias [g, >=n] and c [m, n] are float arrays (c already decoded to its values)."""
+    base = ragged_dot_m(lhs, rhs, group_sizes, lhs_scale, rhs_scale)
+    m, n = base.shape
+    out = alpha * base
+    if c is not None and beta != 0.0:
+        out = out + beta * np.asarray(c, dtype=np.float64)
+    start = 0
+    for h, s in enumerate(np.asarray(group_sizes)):
+        s = max(int(s), 0)
+        s = min(s, m - start)
+        if bias is not None:
+            out[start:start + s] += np.asarray(bias, dtype=np.float64)[h, :n]
+        start += s
+    out[start:] = 0.0
+    return out
+
+
+def ragged_dot_k_epilogue(lhs, dout, group_sizes, alpha=1.0, beta=0.0, c=None):
+    """fp64 out[h] = alpha * (lhs_h^T . dout_h) + beta * c[h] (c [g, k, n] float values)."""
+    out = alpha * ragged_dot_k(lhs, dout, group_sizes)
+    if c is not None and beta != 0.0:
+        out = out + beta * np.asarray(c, dtype=np.float64)
+    return out
+
+
 def ragged_dot_k(lhs, dout, group_sizes, pairs=None):
     """fp64 result of the contracting ragged dot: [g, k, n], or the rows out[g_q, i_q, :]
     for the (g, i) pairs given as an int array of shape [npairs, 2]."""

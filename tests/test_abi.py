@@ -22,7 +22,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for required in ("ragged_dot_m", "ragged_dot_m_nk", "ragged_dot_k", "padded_dot", "gg_workspace_bytes", "gg_schedule",
+    for required in ("ragged_dot_m", "ragged_dot_m_nk", "ragged_dot_m_epilogue", "ragged_dot_k_epilogue", "ragged_dot_k",
+                     "padded_dot", "gg_workspace_bytes", "gg_schedule",
                      "gg_read_device_status", "gg_status_string", "gg_abi_version"):
         assert required in names
 
@@ -34,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert B.abi_version() == 2
+    assert B.abi_version() == 3
     for code in range(8):
         assert B.status_string(code)
 
@@ -79,6 +80,24 @@ def test_ragged_m_nk_host_validation():
     assert nk(k=60) == 6                         # k % 8
     assert nk(n=12) == 6                         # n % 8
     assert nk(wsb=WS_SMALL) == 5
+
+
+def test_epilogue_host_validation():
+    L = B.lib()
+    def me(bias=NULL, stride=0, alpha=1.0, beta=0.0, ind=1, outd=1, gs=P, g=4, k=64):
+        return L.ragged_dot_m_epilogue(P, P, gs, P, 64, k, 64, g, ind, outd, NULL, NULL, bias, stride, alpha, beta, P, 4096,
+                                       None)
+    assert me(bias=P, stride=32) == 2                          # bias row stride below n
+    assert me(bias=ctypes.c_void_p(0x10002), stride=64) == 4   # bias not 4-byte aligned
+    assert me(gs=NULL, alpha=2.0) == 1
+    assert me(g=0, beta=1.0) == 2
+    assert me(ind=0, outd=1, alpha=2.0) == 3                   # fp32 in -> bf16 out
+    assert me(ind=2, k=48, alpha=2.0) == 6
+    def ke(alpha=1.0, beta=0.0, ind=1, outd=0, gs=P, wsb=4096):
+        return L.ragged_dot_k_epilogue(P, P, gs, P, 64, 64, 64, 4, ind, outd, alpha, beta, P, wsb, None)
+    assert ke(gs=NULL, beta=1.0) == 1
+    assert ke(ind=2, beta=1.0) == 3
+    assert ke(beta=1.0, wsb=WS_SMALL) == 5
 
 
 def test_ragged_k_host_validation():

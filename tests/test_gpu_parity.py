@@ -222,6 +222,58 @@ def test_ragged_m_nk(case):
         check_fp32(y32, ref, "nk case 0, fp32 out")
 
 
+# ---- fused epilogue: out = alpha * acc + bias[h] + beta * out -----------------------------
+
+def test_m_epilogue_bias_alpha_beta():
+    m, k, n, gs = 640, 512, 400, [0, 37, 256, 1, 300, 6]   # 600 routed rows: the last 40 stay 0
+    say("ragged_m epilogue", m, k, n, len(gs))
+    d = to_dev(W.small_inputs("m", "bf16", m, k, n, gs, seed=70))
+    gen = torch.Generator().manual_seed(70)
+    bias = torch.randn(len(gs), n + 24, generator=gen)[:, :n].to(DEV)   # row stride n + 24
+    for out_dtype in (torch.bfloat16, torch.float32):
+        c = torch.randn(m, n, generator=gen).to(out_dtype).to(DEV)
+        out = c.clone()
+        y = gg().ragged_dot_m(d["lhs"], d["rhs"], d["group_sizes"], out=out, bias=bias, alpha=0.5, beta=1.0)
+        torch.cuda.synchronize()
+        ref = oracle.ragged_dot_m_epilogue(raw(d["lhs"]), raw(d["rhs"]), gs, bias=bias.cpu().numpy(), alpha=0.5, beta=1.0,
+                                           c=c.double().cpu().numpy())
+        (check_bf16 if out_dtype == torch.bfloat16 else check_fp32)(y, ref, f"epilogue {out_dtype}")
+        assert torch.all(y[sum(gs):] == 0)
+
+
+def test_m_epilogue_mxfp8_bias():
+    m, k, n, gs = MX_RING_CASES[0]
+    say("ragged_m mxfp8 epilogue", m, k, n, len(gs))
+    d = to_dev(W.small_inputs("m", "mxfp8", m, k, n, gs, seed=71))
+    bias = torch.randn(len(gs), n, generator=torch.Generator().manual_seed(71)).to(DEV)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    y = gg().ragged_dot_m(d["lhs"], d["rhs"], d["group_sizes"], out=out, lhs_scale=d["lhs_scale"],
+                          rhs_scale=d["rhs_scale"], bias=bias, alpha=2.0)
+    torch.cuda.synchronize()
+    ref = oracle.ragged_dot_m_epilogue(raw(d["lhs"]), raw(d["rhs"]), gs, bias=bias.cpu().numpy(), alpha=2.0,
+                                       lhs_scale=raw(d["lhs_scale"]), rhs_scale=raw(d["rhs_scale"]))
+    check_bf16(y, ref, "mx epilogue")
+
+
+def test_k_epilogue_accumulates():
+    m, k, n, gs = 2048, 640, 1280, [700, 0, 1, 1000, 347]
+    say("ragged_k epilogue", m, k, n, len(gs))
+    d = to_dev(W.small_inputs("k", "bf16", m, k, n, gs, seed=72))
+    c = torch.randn(len(gs), k, n, generator=torch.Generator().manual_seed(72)).to(DEV)
+    out = c.clone()
+    y = gg().ragged_dot_k(d["lhs"], d["dout"], d["group_sizes"], out=out, alpha=1.0, beta=1.0)
+    torch.cuda.synchronize()
+    ref = oracle.ragged_dot_k_epilogue(raw(d["lhs"]), raw(d["dout"]), gs, beta=1.0, c=c.double().cpu().numpy())
+    check_fp32(y, ref, "k epilogue, beta 1")
+    assert torch.equal(y[1], c[1])   # empty group: beta * out exactly
+
+
+def test_epilogue_unsupported_path_raises():
+    d = to_dev(W.small_inputs("m", "f32", 64, 32, 64, [64], seed=73))
+    with pytest.raises(gg().GGError):
+        gg().ragged_dot_m(d["lhs"], d["rhs"], d["group_sizes"], alpha=2.0)
+
+
 def test_device_status_and_clamping():
     say("invalid group sizes")
     m, k, n = 200, 64, 64

@@ -233,6 +233,53 @@ def test_m_nk_is_the_data_gradient_of_m():
     assert math.isclose(lhs_side, rhs_side, rel_tol=1e-12, abs_tol=1e-12)
 
 
+def test_m_epilogue_bias_alpha_brute_force():
+    """bias[h] is added to every row of group h, alpha scales the product; rows past the
+    groups' total stay 0 (written out plainly)."""
+    m, k, n, gs = 9, 3, 4, [3, 0, 4]
+    r = np.random.default_rng(13)
+    lhs, rhs = _f32(r.standard_normal((m, k))), _f32(r.standard_normal((len(gs), k, n)))
+    bias = _f32(r.standard_normal((len(gs), n + 2)))   # row stride n + 2: only the first n used
+    out = oracle.ragged_dot_m_epilogue(lhs, rhs, gs, bias=bias, alpha=-0.5)
+    row = 0
+    for h, s in enumerate(gs):
+        for _ in range(s):
+            for j in range(n):
+                acc = sum(float(lhs[row, t]) * float(rhs[h, t, j]) for t in range(k))
+                assert math.isclose(out[row, j], -0.5 * acc + float(bias[h, j]), rel_tol=1e-13, abs_tol=1e-13)
+            row += 1
+    assert np.all(out[sum(gs):] == 0.0)
+
+
+def test_m_epilogue_beta_accumulates_split_k():
+    """beta = 1 on a first partial product gives the whole product: the sum over k split in
+    two parts equals the sum over all of k."""
+    m, k, n, gs = 17, 10, 6, [5, 0, 12]
+    r = np.random.default_rng(14)
+    lhs, rhs = _f32(r.standard_normal((m, k))), _f32(r.standard_normal((len(gs), k, n)))
+    first = oracle.ragged_dot_m(lhs[:, :4], rhs[:, :4], gs)
+    both = oracle.ragged_dot_m_epilogue(lhs[:, 4:], rhs[:, 4:], gs, beta=1.0, c=first)
+    np.testing.assert_allclose(both, oracle.ragged_dot_m(lhs, rhs, gs), rtol=1e-12, atol=1e-12)
+
+
+def test_k_epilogue_beta_is_gradient_accumulation():
+    """Two micro-batches accumulated with beta = 1 give the weight gradient of their union,
+    each group's rows of both batches taken together."""
+    k, n = 4, 5
+    gs1, gs2 = [3, 0, 2], [1, 4, 0]
+    r = np.random.default_rng(15)
+    a1, d1 = _f32(r.standard_normal((sum(gs1), k))), _f32(r.standard_normal((sum(gs1), n)))
+    a2, d2 = _f32(r.standard_normal((sum(gs2), k))), _f32(r.standard_normal((sum(gs2), n)))
+    acc = oracle.ragged_dot_k_epilogue(a2, d2, gs2, beta=1.0, c=oracle.ragged_dot_k(a1, d1, gs1))
+    rows_a, rows_d, s1, s2 = [], [], 0, 0
+    for h in range(3):
+        rows_a += [a1[s1:s1 + gs1[h]], a2[s2:s2 + gs2[h]]]
+        rows_d += [d1[s1:s1 + gs1[h]], d2[s2:s2 + gs2[h]]]
+        s1 += gs1[h]; s2 += gs2[h]
+    union = oracle.ragged_dot_k(np.concatenate(rows_a), np.concatenate(rows_d), [a + b for a, b in zip(gs1, gs2)])
+    np.testing.assert_allclose(acc, union, rtol=1e-12, atol=1e-12)
+
+
 def test_k_pairs_select_rows_of_the_full_result():
     m, k, n, gs = 14, 5, 3, [3, 0, 11]
     r = np.random.default_rng(11)
