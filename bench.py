@@ -58,8 +58,8 @@ def algorithmic_bytes(w, gs):
     osz = 4 if w.out_dtype == "f32" else 2
     S = int(np.sum(gs))
     nonempty = int(np.sum(np.asarray(gs) > 0))
-    if w.op in ("m", "m_nk"):
-        b = w.m * w.k * esz + nonempty * w.k * w.n * esz + w.m * w.n * osz
+    if w.op in ("m", "m_nk", "m_gated"):
+        b = w.m * w.k * esz + nonempty * w.k * w.n * esz * (2 if w.op == "m_gated" else 1) + w.m * w.n * osz
         if w.in_dtype == "mxfp8":
             b += w.m * (w.k // 32) + nonempty * (w.k // 32) * w.n
         return b
@@ -67,7 +67,7 @@ def algorithmic_bytes(w, gs):
 
 
 def useful_flops(w, gs):
-    return 2.0 * float(np.sum(gs)) * w.k * w.n
+    return 2.0 * float(np.sum(gs)) * w.k * w.n * (2 if w.op == "m_gated" else 1)
 
 
 def time_calls(fn, steps, warmup, torch):
@@ -103,6 +103,11 @@ def cpu_baseline(w, d, gs, target_s, W, torch):
         rs = raw(d["rhs_scale"]) if "rhs_scale" in d else None
         per_unit = 2.0 * w.k * w.n
         run = lambda cnt: oracle.ragged_dot_m(lhs, rhs, gsn, ls, rs, rows=rng.integers(0, S, cnt))
+        unit = "rows"
+    elif w.op == "m_gated":
+        w0, w1 = raw(d["w0"]), raw(d["w1"])
+        per_unit = 4.0 * w.k * w.n
+        run = lambda cnt: oracle.ragged_dot_m_gated(lhs, w0, w1, gsn, rows=rng.integers(0, S, cnt))
         unit = "rows"
     elif w.op == "m_nk":
         rhs_kn = np.ascontiguousarray(np.swapaxes(raw(d["rhs"]), 1, 2))   # once, outside the timed sample
@@ -239,7 +244,11 @@ def main():
     F = useful_flops(w, gs)
     B = algorithmic_bytes(w, gs)
 
-    if w.op in ("m", "m_nk"):
+    if w.op == "m_gated":
+        out = torch.empty((w.m, w.n), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(G.workspace_bytes("ragged_m", w.m, w.k, w.n, w.g), dtype=torch.uint8, device=dev)
+        fn = lambda: G.ragged_dot_m_gated(d["lhs"], d["w0"], d["w1"], d["group_sizes"], act="silu", out=out, workspace=ws)
+    elif w.op in ("m", "m_nk"):
         out_dtype = torch.float32 if w.out_dtype == "f32" else torch.bfloat16
         out = torch.empty((w.m, w.n), dtype=out_dtype, device=dev)
         ws = torch.empty(G.workspace_bytes("ragged_m", w.m, w.k, w.n, w.g), dtype=torch.uint8, device=dev)
@@ -272,8 +281,8 @@ def main():
               "useful_gflop_per_step": F / 1e9, "algorithmic_mb_per_step": B / 1e6,
               "kernel_us_per_launch": per_launch * 1e6}
 
-    if not a.no_padded and w.op == "m_nk":
-        config["padded"] = None   # padded_dot takes [g,k,n] weights only
+    if not a.no_padded and w.op in ("m_nk", "m_gated"):
+        config["padded"] = None   # padded_dot is the plain [g,k,n] product only
     elif not a.no_padded:
         cap = int(math.ceil(gs.max() / 256.0) * 256)
         pws = torch.empty(G.workspace_bytes(f"padded_{w.op}", w.m, w.k, w.n, w.g, cap, d["lhs"].dtype),

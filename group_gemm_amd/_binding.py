@@ -43,6 +43,8 @@ def lib():
                                             i64, f32, f32, vp, sz, vp]
         L.ragged_dot_k_epilogue.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, ctypes.c_int, f32, f32, vp,
                                             sz, vp]
+        L.ragged_dot_m_gated.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         vp, vp, i64, vp, sz, vp]
         L.padded_dot.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i32, i64, ctypes.c_int, ctypes.c_int,
                                  vp, vp, vp, sz, vp]
         L.gg_schedule.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
@@ -50,7 +52,8 @@ def lib():
         L.gg_status_string.argtypes = [ctypes.c_int]
         L.gg_status_string.restype = ctypes.c_char_p
         L.gg_abi_version.restype = ctypes.c_int
-        for f in ("ragged_dot_m", "ragged_dot_m_nk", "ragged_dot_m_epilogue", "ragged_dot_k", "ragged_dot_k_epilogue",
+        for f in ("ragged_dot_m", "ragged_dot_m_nk", "ragged_dot_m_epilogue", "ragged_dot_m_gated", "ragged_dot_k",
+                  "ragged_dot_k_epilogue",
                   "padded_dot", "gg_schedule", "gg_read_device_status"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -139,6 +142,38 @@ def ragged_dot_m(lhs, rhs, group_sizes, out=None, out_dtype=None, lhs_scale=None
                               GG_DT[out.dtype], _p(lhs_scale), _p(rhs_scale), _p(ws), ws.numel(),
                               _stream(lhs.device))
     _check(code, "ragged_dot_m")
+    return out
+
+
+ACT = {"silu": 0, "gelu_tanh": 1}
+
+
+def ragged_dot_m_gated(lhs, w0, w1, group_sizes, act="silu", out=None, out_dtype=torch.bfloat16, bias0=None, bias1=None,
+                       workspace=None):
+    """out[m,n] = act(lhs . w0[h] + bias0[h]) * (lhs . w1[h] + bias1[h]) for the rows of group h
+    (the fused gate/up projection); rows past sum(group_sizes) are 0.  bf16 lhs [m,k] and
+    w0 / w1 [g,k,n]; biases fp32 [g, >=n] sharing one row stride, or None."""
+    m, k = lhs.shape
+    g, k2, n = w0.shape
+    if w1.shape != w0.shape or k2 != k or group_sizes.shape != (g,) or group_sizes.dtype != torch.int32:
+        raise ValueError("shape/dtype mismatch")
+    if act not in ACT:
+        raise ValueError(f"act must be one of {sorted(ACT)}")
+    stride = 0
+    for b in (bias0, bias1):
+        if b is not None:
+            if b.dtype != torch.float32 or b.dim() != 2 or b.shape[0] != g or b.shape[1] < n or b.stride(1) != 1:
+                raise ValueError("biases must be float32 [g, >=n] with unit column stride")
+            if stride and b.stride(0) != stride:
+                raise ValueError("bias0 and bias1 must share one row stride")
+            stride = b.stride(0)
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=lhs.device)
+    ws = _workspace("ragged_m", m, k, n, g, 0, lhs.dtype, lhs.device, workspace)
+    code = lib().ragged_dot_m_gated(_p(lhs), _p(w0), _p(w1), _p(group_sizes), _p(out), m, k, n, g, GG_DT[lhs.dtype],
+                                    GG_DT[out.dtype], ACT[act], _p(bias0), _p(bias1), stride, _p(ws), ws.numel(),
+                                    _stream(lhs.device))
+    _check(code, "ragged_dot_m_gated")
     return out
 
 

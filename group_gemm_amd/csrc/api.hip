@@ -268,6 +268,33 @@ gg_status ragged_dot_k_epilogue(const void* lhs, const void* dout, const int32_t
                  (hipStream_t)stream, ep);
 }
 
+gg_status ragged_dot_m_gated(const void* lhs, const void* w0, const void* w1, const int32_t* group_sizes, void* out,
+                             int64_t m, int64_t k, int64_t n, int32_t g, gg_dtype in_dtype, gg_dtype out_dtype,
+                             gg_activation act, const float* bias0, const float* bias1, int64_t bias_stride,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    gg_status st = check_common(m, k, n, g, group_sizes, workspace, workspace_bytes, kHeader);
+    if (st != GG_OK) return st;
+    if (in_dtype != GG_DT_BF16) return GG_ERR_UNSUPPORTED;
+    if (!m_dtypes_ok(in_dtype, out_dtype)) return GG_ERR_BAD_DTYPE;
+    if (act != GG_ACT_SILU && act != GG_ACT_GELU_TANH) return GG_ERR_UNSUPPORTED;
+    if ((m * k > 0 && !lhs) || (k * n > 0 && (!w0 || !w1)) || (m * n > 0 && !out)) return GG_ERR_NULL_PTR;
+    if ((bias0 || bias1) && bias_stride < n) return GG_ERR_BAD_SHAPE;
+    if (!aligned(bias0, 4) || !aligned(bias1, 4)) return GG_ERR_MISALIGNED;
+    if (!aligned(lhs, 16) || !aligned(w0, 16) || !aligned(w1, 16) || !aligned(out, 16)) return GG_ERR_MISALIGNED;
+    if (k % 8 != 0 || n % 8 != 0) return GG_ERR_UNSUPPORTED;
+    int cus;
+    if (device_cus(&cus) != 0) return GG_ERR_HIP;
+    gg::GParams p{};
+    p.lhs = lhs; p.w0 = w0; p.w1 = w1; p.group_sizes = group_sizes; p.out = out; p.status = (uint32_t*)workspace;
+    p.bias0 = bias0; p.bias1 = bias1; p.bias_stride = bias_stride;
+    p.m = (int)m; p.k = (int)k; p.n = (int)n; p.g = g; p.out_f32 = out_dtype == GG_DT_F32; p.act = (int)act;
+    if (!gg::ragged_m_gated_ok(p)) return GG_ERR_UNSUPPORTED;
+    const int64_t bound = (cdiv64(m, 256) + g + 1) * cdiv64(n, 128);
+    if (!fits_i32(bound)) return GG_ERR_BAD_SHAPE;
+    return gg::launch_ragged_m_gated(p, persistent_grid(bound, 1, cus), (hipStream_t)stream) == hipSuccess ? GG_OK
+                                                                                                           : GG_ERR_HIP;
+}
+
 gg_status ragged_dot_k(const void* lhs, const void* dout, const int32_t* group_sizes, void* out, int64_t m, int64_t k,
                        int64_t n, int32_t g, gg_dtype in_dtype, gg_dtype out_dtype, void* workspace,
                        size_t workspace_bytes, void* stream) {

@@ -43,6 +43,24 @@ struct KParams {
     float alpha, beta;
 };
 
+// Fused gate/up projection: out[m,n] = act(lhs . w0[h] + b0[h]) * (lhs . w1[h] + b1[h]).
+struct GParams {
+    const void* lhs;            // [m,k]
+    const void* w0;             // [g,k,n] gate weights
+    const void* w1;             // [g,k,n] up weights
+    const int32_t* group_sizes;
+    void* out;                  // [m,n]
+    uint32_t* status;
+    const float* bias0;         // [g, bias_stride] or NULL
+    const float* bias1;
+    int64_t bias_stride;
+    int m, k, n, g;
+    int out_f32;
+    int act;                    // gg_activation
+};
+bool ragged_m_gated_ok(const GParams& p);
+hipError_t launch_ragged_m_gated(const GParams& p, int grid, hipStream_t s);
+
 // Kernel families.  Each launcher returns the hipError_t of its launch.
 hipError_t launch_ragged_m_bf16(const MParams& p, int grid, bool vec, hipStream_t s);
 // vectorised bf16 kernel (16-byte aligned operands, k % 8 == 0, n % 8 == 0)

@@ -62,12 +62,16 @@ WORKLOADS = {
         # output gradient [8192, 14336] times each expert's stored weights [4096, 14336]^T
         Workload(7, "mixtral8x7b_dgrad_bf16", "m_nk", "bf16", "bf16", 8192, 14336, 4096, 8,
                  "topk_normal_logits", tokens=4096, top_k=2),
+        # the same up-projection as a fused gate/up pair with SiLU: two [8, 4096, 14336]
+        # weight tensors, one [8192, 14336] intermediate
+        Workload(8, "mixtral8x7b_gated_bf16", "m_gated", "bf16", "bf16", 8192, 4096, 14336, 8,
+                 "topk_normal_logits", tokens=4096, top_k=2),
     ]
 }
 
 # the MXFP8 and data-gradient workloads reuse the bf16 forward one's routing stream, so all
 # three see the same sizes
-_ROUTING_WID = {4: 2, 7: 2}
+_ROUTING_WID = {4: 2, 7: 2, 8: 2}
 
 
 def rng(wid: int, stream: int, seed: int = 0) -> np.random.Generator:
@@ -193,6 +197,13 @@ def make_inputs(w: Workload, device="cpu", seed: int = 0, gs: np.ndarray | None 
     elif w.op == "k":
         out["lhs"] = _randn((m, k), w.wid, 1, seed, device).to(torch.bfloat16)
         out["dout"] = _randn((m, n), w.wid, 2, seed, device).to(torch.bfloat16)
+    elif w.op == "m_gated":
+        out["lhs"] = _randn((m, k), w.wid, 1, seed, device).to(torch.bfloat16)
+        for key, stream in (("w0", 2), ("w1", 3)):
+            wt = torch.empty((g, k, n), device=device, dtype=torch.bfloat16)
+            for h in range(g):
+                wt[h] = _randn((k, n), w.wid, stream, seed * 65536 + h, device, std=1 / math.sqrt(k)).to(torch.bfloat16)
+            out[key] = wt
     elif w.op == "m_nk":
         out["lhs"] = _randn((m, k), w.wid, 1, seed, device).to(torch.bfloat16)
         rhs = torch.empty((g, n, k), device=device, dtype=torch.bfloat16)
@@ -260,5 +271,7 @@ def to_numpy_raw(t: torch.Tensor) -> np.ndarray:
 
 
 def useful_flops(w: Workload, gs) -> float:
-    """2 * sum(m_g) * k * n, the only work credited to the ragged dot."""
-    return 2.0 * float(np.sum(np.maximum(gs, 0))) * w.k * w.n
+    """2 * sum(m_g) * k * n, the only work credited to the ragged dot (twice that for the
+    fused gate/up pair, which computes two products)."""
+    f = 2.0 * float(np.sum(np.maximum(gs, 0))) * w.k * w.n
+    return 2.0 * f if w.op == "m_gated" else f

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define GG_ABI_VERSION 3
+#define GG_ABI_VERSION 4
 
 typedef enum {
     GG_OK = 0,
@@ -65,6 +65,11 @@ typedef enum {
     GG_OP_PADDED_M = 2,            /* padded_dot, non-contracting form                      */
     GG_OP_PADDED_K = 3             /* padded_dot, contracting form                          */
 } gg_op;
+
+typedef enum {
+    GG_ACT_SILU = 0,               /* x * sigmoid(x)  (SwiGLU when applied to the gate)     */
+    GG_ACT_GELU_TANH = 1           /* 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))       */
+} gg_activation;
 
 /* Device status bits (read back with gg_read_device_status). */
 #define GG_DEV_NEGATIVE_SIZE 0x1u  /* some group_sizes[h] < 0 (treated as 0)               */
@@ -137,6 +142,23 @@ gg_status ragged_dot_k_epilogue(const void* lhs, const void* dout, const int32_t
                                 int64_t m, int64_t k, int64_t n, int32_t g, gg_dtype in_dtype,
                                 gg_dtype out_dtype, float alpha, float beta, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* ragged_dot_m_gated -- the fused gate/up projection of an MoE expert block:
+ *   out[r, :] = act(lhs[r, :] . w0[h] + bias0[h, :]) * (lhs[r, :] . w1[h] + bias1[h, :])
+ * for every row r of group h; rows r >= sum(sizes) are 0.
+ * ("Group-GEMM in XLA", Part 1: the dense formulation's gate/up einsums and
+ * activation(layer_w0) * layer_w1; Part 4: the MaxText layer's gmm_up(x, w0, w1, w0_bias,
+ * w1_bias) followed by apply_ffn_activation, fused here into one pass.)
+ *   lhs [m, k], w0 / w1 [g, k, n]: bf16; out [m, n]: bf16 or fp32.
+ *   bias0 / bias1: fp32 [g, bias_stride] (bias_stride >= n, 4-byte aligned) or NULL.
+ *   act: GG_ACT_SILU or GG_ACT_GELU_TANH.
+ * Requires 16-byte aligned lhs, w0, w1, out and k % 8 == 0, n % 8 == 0; other shapes
+ * return GG_ERR_UNSUPPORTED.  Workspace, status and errors as ragged_dot_m. */
+gg_status ragged_dot_m_gated(const void* lhs, const void* w0, const void* w1, const int32_t* group_sizes,
+                             void* out, int64_t m, int64_t k, int64_t n, int32_t g, gg_dtype in_dtype,
+                             gg_dtype out_dtype, gg_activation act, const float* bias0,
+                             const float* bias1, int64_t bias_stride, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* ragged_dot_k -- contracting ragged dot, the weight-gradient case: the contracted
  * dimension m is ragged and the group index appears in the output.

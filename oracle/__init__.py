@@ -12,6 +12,8 @@ Hurts: Padded-Dot"; Part 3 "Non-Contracting (the MoE Case)" and "Contracting".
 import ctypes
 import os
 
+import math
+
 import numpy as np
 
 from . import build as _build
@@ -125,6 +127,49 @@ def ragged_dot_k_epilogue(lhs, dout, group_sizes, alpha=1.0, beta=0.0, c=None):
     out = alpha * ragged_dot_k(lhs, dout, group_sizes)
     if c is not None and beta != 0.0:
         out = out + beta * np.asarray(c, dtype=np.float64)
+    return out
+
+
+def silu(x):
+    """x * sigmoid(x) = x / (1 + e^-x), in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def gelu_tanh(x):
+    """The tanh form of GELU: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+ACTIVATIONS = {"silu": silu, "gelu_tanh": gelu_tanh}
+
+
+def ragged_dot_m_gated(lhs, w0, w1, group_sizes, act="silu", bias0=None, bias1=None, rows=None):
+    """fp64 gated projection of an MoE expert block ("Group-GEMM in XLA", Part 1: the gate and
+    up einsums over w0 and w1, then activation(layer_w0) * layer_w1; Part 4: gmm_up with both
+    weights and biases, then the FFN activation):
+    out[r, :] = act(lhs[r, :] . w0[h] + bias0[h, :n]) * (lhs[r, :] . w1[h] + bias1[h, :n]),
+    rows past the groups' total 0; `rows` selects output rows as in ragged_dot_m."""
+    gate = ragged_dot_m(lhs, w0, group_sizes, rows=rows)
+    up = ragged_dot_m(lhs, w1, group_sizes, rows=rows)
+    m = np.asarray(lhs).shape[0]
+    n = gate.shape[1]
+    gs = np.asarray(group_sizes)
+    # the group of every output row under the clamping reading (-1: past the total)
+    grp = np.full(m, -1, dtype=np.int64)
+    start = 0
+    for h, s in enumerate(gs):
+        s = min(max(int(s), 0), m - start)
+        grp[start:start + s] = h
+        start += s
+    sel = grp if rows is None else grp[np.asarray(rows, dtype=np.int64)]
+    if bias0 is not None:
+        gate = gate + np.where(sel[:, None] >= 0, np.asarray(bias0, dtype=np.float64)[np.maximum(sel, 0), :n], 0.0)
+    if bias1 is not None:
+        up = up + np.where(sel[:, None] >= 0, np.asarray(bias1, dtype=np.float64)[np.maximum(sel, 0), :n], 0.0)
+    out = ACTIVATIONS[act](gate) * up
+    out[sel < 0] = 0.0
     return out
 
 

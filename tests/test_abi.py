@@ -22,7 +22,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for required in ("ragged_dot_m", "ragged_dot_m_nk", "ragged_dot_m_epilogue", "ragged_dot_k_epilogue", "ragged_dot_k",
+    for required in ("ragged_dot_m", "ragged_dot_m_nk", "ragged_dot_m_epilogue", "ragged_dot_k_epilogue", "ragged_dot_m_gated",
+                     "ragged_dot_k",
                      "padded_dot", "gg_workspace_bytes", "gg_schedule",
                      "gg_read_device_status", "gg_status_string", "gg_abi_version"):
         assert required in names
@@ -35,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert B.abi_version() == 3
+    assert B.abi_version() == 4
     for code in range(8):
         assert B.status_string(code)
 
@@ -98,6 +99,19 @@ def test_epilogue_host_validation():
     assert ke(gs=NULL, beta=1.0) == 1
     assert ke(ind=2, beta=1.0) == 3
     assert ke(beta=1.0, wsb=WS_SMALL) == 5
+
+
+def test_gated_host_validation():
+    L = B.lib()
+    def gt(w1=P, act=0, ind=1, outd=1, b0=NULL, stride=0, k=64, gs=P):
+        return L.ragged_dot_m_gated(P, P, w1, gs, P, 64, k, 64, 4, ind, outd, act, b0, NULL, stride, P, 4096, None)
+    assert gt(gs=NULL) == 1
+    assert gt(w1=NULL) == 1
+    assert gt(ind=0, outd=0) == 6            # fp32 not offered
+    assert gt(act=7) == 6
+    assert gt(b0=P, stride=8) == 2           # bias stride below n
+    assert gt(w1=ctypes.c_void_p(0x10008)) == 4
+    assert gt(k=60) == 6
 
 
 def test_ragged_k_host_validation():

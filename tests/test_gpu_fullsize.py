@@ -82,6 +82,24 @@ def test_full_size_ragged_m_nk():
     assert not bad.any(), f"{w.name}: {int(bad.sum())} of {bad.size} sampled elements outside the bf16 bar"
 
 
+def test_full_size_ragged_m_gated():
+    """The fused gate/up workload (SiLU), sampled rows against the oracle."""
+    import group_gemm_amd as G
+    w = W.WORKLOADS["mixtral8x7b_gated_bf16"]
+    say("full size", w.name)
+    gs = W.group_sizes(w)
+    d = W.make_inputs(w, device=DEV, gs=gs)
+    out = torch.full((w.m, w.n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    G.ragged_dot_m_gated(d["lhs"], d["w0"], d["w1"], d["group_sizes"], act="silu", out=out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()), "non-finite output"
+    rows = sample_rows(gs, np.random.default_rng(w.wid))
+    ref = oracle.ragged_dot_m_gated(raw(d["lhs"]), raw(d["w0"]), raw(d["w1"]), gs, act="silu", rows=rows)
+    y = out[torch.from_numpy(rows).to(DEV)].double().cpu().numpy()
+    bad = np.abs(y - ref) > 1e-2 * np.abs(ref) + 1e-2
+    assert not bad.any(), f"{w.name}: {int(bad.sum())} of {bad.size} sampled elements outside the bf16 bar"
+
+
 def test_full_size_ragged_k():
     import group_gemm_amd as G
     w = W.WORKLOADS["llama4scout_wgrad_bf16"]

@@ -222,6 +222,39 @@ def test_ragged_m_nk(case):
         check_fp32(y32, ref, "nk case 0, fp32 out")
 
 
+# ---- fused gate/up projection: act(x . w0 + b0) * (x . w1 + b1) ------------------------------
+
+GATED_CASES = [
+    (640, 512, 400, [0, 37, 256, 1, 300, 6], "silu"),    # 600 routed rows, partial 128-column tile
+    (513, 96, 136, [257, 256], "gelu_tanh"),
+    (300, 264, 256, [100, 0, 150, 50], "silu"),            # k tail
+]
+
+
+@pytest.mark.parametrize("case", range(len(GATED_CASES)))
+def test_ragged_m_gated(case):
+    m, k, n, gs, act = GATED_CASES[case]
+    say("ragged_m_gated", m, k, n, len(gs), act)
+    d = to_dev(W.small_inputs("m", "bf16", m, k, n, gs, seed=80 + case))
+    w1 = to_dev(W.small_inputs("m", "bf16", m, k, n, gs, seed=90 + case))["rhs"]
+    gen = torch.Generator().manual_seed(80 + case)
+    b0 = torch.randn(len(gs), n + 8, generator=gen)[:, :n].to(DEV) if case != 1 else None
+    b1 = torch.randn(len(gs), n + 8, generator=gen)[:, :n].to(DEV) if case != 1 else None
+    ref = oracle.ragged_dot_m_gated(raw(d["lhs"]), raw(d["rhs"]), raw(w1), gs, act=act,
+                                    bias0=None if b0 is None else b0.cpu().numpy(),
+                                    bias1=None if b1 is None else b1.cpu().numpy())
+    out = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    y = gg().ragged_dot_m_gated(d["lhs"], d["rhs"], w1, d["group_sizes"], act=act, out=out, bias0=b0, bias1=b1)
+    torch.cuda.synchronize()
+    check_bf16(y, ref, f"gated case {case}")
+    assert torch.all(y[sum(gs):] == 0)
+    if case == 0:
+        y32 = gg().ragged_dot_m_gated(d["lhs"], d["rhs"], w1, d["group_sizes"], act=act, out_dtype=torch.float32,
+                                      bias0=b0, bias1=b1)
+        torch.cuda.synchronize()
+        check_fp32(y32, ref, "gated case 0, fp32 out")
+
+
 # ---- fused epilogue: out = alpha * acc + bias[h] + beta * out -----------------------------
 
 def test_m_epilogue_bias_alpha_beta():

@@ -280,6 +280,43 @@ def test_k_epilogue_beta_is_gradient_accumulation():
     np.testing.assert_allclose(acc, union, rtol=1e-12, atol=1e-12)
 
 
+def test_activations_match_library_routines():
+    """silu against x * expit(x) (scipy) and the tanh GELU against torch's, over a wide range;
+    silu(0) = 0 and silu(x) -> x, 0 at the ends."""
+    from scipy.special import expit
+    x = np.linspace(-30.0, 30.0, 2001)
+    np.testing.assert_allclose(oracle.silu(x), x * expit(x), rtol=1e-14, atol=1e-300)
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    np.testing.assert_allclose(oracle.gelu_tanh(x), ref, rtol=1e-13, atol=1e-15)
+    assert oracle.silu(0.0) == 0.0 and abs(oracle.silu(40.0) - 40.0) < 1e-12 and abs(oracle.silu(-40.0)) < 1e-12
+
+
+@pytest.mark.parametrize("act", ["silu", "gelu_tanh"])
+def test_gated_brute_force(act):
+    """act(x . w0[h] + b0[h]) * (x . w1[h] + b1[h]) written out with loops; rows past the
+    total are 0."""
+    m, k, n, gs = 8, 3, 4, [2, 0, 5]
+    r = np.random.default_rng(16)
+    lhs = _f32(r.standard_normal((m, k)))
+    w0, w1 = _f32(r.standard_normal((3, k, n))), _f32(r.standard_normal((3, k, n)))
+    b0, b1 = _f32(r.standard_normal((3, n + 1))), _f32(r.standard_normal((3, n + 1)))
+    out = oracle.ragged_dot_m_gated(lhs, w0, w1, gs, act=act, bias0=b0, bias1=b1)
+    f = {"silu": lambda v: v / (1.0 + math.exp(-v)),
+         "gelu_tanh": lambda v: 0.5 * v * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (v + 0.044715 * v ** 3)))}[act]
+    row = 0
+    for h, s in enumerate(gs):
+        for _ in range(s):
+            for j in range(n):
+                gate = sum(float(lhs[row, t]) * float(w0[h, t, j]) for t in range(k)) + float(b0[h, j])
+                up = sum(float(lhs[row, t]) * float(w1[h, t, j]) for t in range(k)) + float(b1[h, j])
+                assert math.isclose(out[row, j], f(gate) * up, rel_tol=1e-12, abs_tol=1e-12)
+            row += 1
+    assert np.all(out[sum(gs):] == 0.0)
+    rows = np.array([7, 0, 3])
+    np.testing.assert_array_equal(oracle.ragged_dot_m_gated(lhs, w0, w1, gs, act=act, bias0=b0, bias1=b1, rows=rows),
+                                  out[rows])
+
+
 def test_k_pairs_select_rows_of_the_full_result():
     m, k, n, gs = 14, 5, 3, [3, 0, 11]
     r = np.random.default_rng(11)
