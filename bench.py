@@ -56,6 +56,10 @@ def algorithmic_bytes(w, gs):
     """Inputs read once (weights only of non-empty groups) plus the output written once."""
     esz = {"bf16": 2, "f32": 4, "mxfp8": 1}[w.in_dtype]
     osz = 4 if w.out_dtype == "f32" else 2
+    if w.op == "permute":   # token rows and ids read once; sorted rows, both index maps, sizes written
+        return w.tokens * w.k * esz + w.m * 4 + w.m * w.k * esz + 2 * w.m * 4 + w.g * 4
+    if w.op == "unpermute":   # sorted rows, inverse order and weights read once; token rows written
+        return w.m * w.n * esz + w.m * 4 + w.m * 4 + w.tokens * w.n * osz
     S = int(np.sum(gs))
     nonempty = int(np.sum(np.asarray(gs) > 0))
     if w.op in ("m", "m_nk", "m_gated"):
@@ -67,6 +71,10 @@ def algorithmic_bytes(w, gs):
 
 
 def useful_flops(w, gs):
+    if w.op == "permute":
+        return 0.0
+    if w.op == "unpermute":   # one multiply-add per element of every routed row
+        return 2.0 * w.m * w.n
     return 2.0 * float(np.sum(gs)) * w.k * w.n * (2 if w.op == "m_gated" else 1)
 
 
@@ -93,6 +101,8 @@ def cpu_baseline(w, d, gs, target_s, W, torch):
     output rows (m-ragged) or (group, k-index) rows (k-ragged); rate in TFLOP/s."""
     import oracle
     raw = W.to_numpy_raw
+    if w.op in ("permute", "unpermute"):
+        return cpu_baseline_routing(w, d, target_s, raw, oracle)
     lhs = raw(d["lhs"])
     gsn = raw(d["group_sizes"])
     S = int(gsn.sum())
@@ -134,6 +144,27 @@ def cpu_baseline(w, d, gs, target_s, W, torch):
             cnt *= 2
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(oracle.num_threads()), "kind": "oracle",
             "sample": f"{done} {unit} of the {w.name} workload drawn uniformly, fp64 oracle, {spent:.1f} s"}
+
+
+def cpu_baseline_routing(w, d, target_s, raw, oracle):
+    """The oracle's permute / un-permute over the whole workload, repeated until about
+    target_s seconds are spent; rate in GB/s of the same algorithmic bytes."""
+    if w.op == "permute":
+        x, experts = raw(d["x"]), raw(d["experts"])
+        run = lambda: oracle.moe_permute(x, experts, w.g)
+    else:
+        y, weights = raw(d["y"]), raw(d["weights"])
+        c2s = oracle.moe_permute(np.zeros((w.tokens, 1), np.float32), raw(d["experts"]), w.g)[4]
+        run = lambda: oracle.moe_unpermute(y, c2s, weights)
+    B = algorithmic_bytes(w, None)
+    spent, done = 0.0, 0
+    while spent < target_s:
+        t0 = time.perf_counter()
+        run()
+        spent += time.perf_counter() - t0
+        done += 1
+    return {"value": B * done / spent / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} whole {w.name} calls, numpy oracle (single-threaded), {spent:.1f} s"}
 
 
 def kernels_digest():
@@ -244,7 +275,18 @@ def main():
     F = useful_flops(w, gs)
     B = algorithmic_bytes(w, gs)
 
-    if w.op == "m_gated":
+    if w.op == "permute":
+        ws = torch.empty(G.workspace_bytes("permute", w.m, w.k, 0, w.g), dtype=torch.uint8, device=dev)
+        outs = G.moe_permute(d["x"], d["experts"], w.g, workspace=ws)
+        fn = lambda: G.moe_permute(d["x"], d["experts"], w.g, workspace=ws, out=outs)
+    elif w.op == "unpermute":
+        # the inverse order the permute of the same routing produces (narrow rows: only the
+        # index maps are used)
+        narrow = torch.zeros((w.tokens, 8), dtype=torch.bfloat16, device=dev)
+        c2s = G.moe_permute(narrow, d["experts"], w.g)[4]
+        out = torch.empty((w.tokens, w.n), dtype=torch.bfloat16, device=dev)
+        fn = lambda: G.moe_unpermute(d["y"], c2s, d["weights"], out=out)
+    elif w.op == "m_gated":
         out = torch.empty((w.m, w.n), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(G.workspace_bytes("ragged_m", w.m, w.k, w.n, w.g), dtype=torch.uint8, device=dev)
         fn = lambda: G.ragged_dot_m_gated(d["lhs"], d["w0"], d["w1"], d["group_sizes"], act="silu", out=out, workspace=ws)
@@ -262,26 +304,33 @@ def main():
 
     wall, per_launch = time_calls(fn, a.steps, a.warmup, torch)
     ms_per_step = wall / a.steps * 1e3
-    value = F / (wall / a.steps) / 1e12
+    routing = w.op in ("permute", "unpermute")
+    # pure data movement is rated in GB/s of algorithmic bytes, the products in TFLOP/s
+    value = B / (wall / a.steps) / 1e9 if routing else F / (wall / a.steps) / 1e12
 
     # roofline of the (single) kernel: MFMA-bound if the arithmetic intensity exceeds the
     # ridge point of its precision, else HBM-bound
     peak_f = PEAK_TFLOPS[w.in_dtype]
     ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
-    if F / B >= ridge:
+    if not routing and F / B >= ridge:
         roof = {"bound": "mfma", "achieved": F / per_launch / 1e12, "peak": peak_f, "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": B / per_launch / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_for(w.name)
 
-    config = {"workload": w.name, "op": f"ragged_dot_{w.op}", "m": w.m, "k": w.k, "n": w.n, "g": w.g,
+    config = {"workload": w.name, "op": f"moe_{w.op}" if routing else f"ragged_dot_{w.op}", "m": w.m, "k": w.k,
+              "n": w.n, "g": w.g,
               "group_sizes": {"min": int(gs.min()), "max": int(gs.max()), "sum": int(gs.sum()),
                               "empty": int((gs == 0).sum())},
               "useful_gflop_per_step": F / 1e9, "algorithmic_mb_per_step": B / 1e6,
               "kernel_us_per_launch": per_launch * 1e6}
 
-    if not a.no_padded and w.op in ("m_nk", "m_gated"):
+    if routing:
+        config["tokens"], config["top_k"] = w.tokens, w.top_k
+        if w.op == "permute":
+            config["kernels"] = "histogram, rank, gather (one call; roofline over the whole call)"
+    elif not a.no_padded and w.op in ("m_nk", "m_gated"):
         config["padded"] = None   # padded_dot is the plain [g,k,n] product only
     elif not a.no_padded:
         cap = int(math.ceil(gs.max() / 256.0) * 256)
@@ -298,7 +347,7 @@ def main():
                             "speedup_ragged_vs_padded": p_ms / ms_per_step}
         del pws
 
-    line = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+    line = {"metric": METRIC, "value": value, "unit": "GB/s" if routing else "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
             "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": {"bf16": "bf16", "f32": "f32", "mxfp8": "e4m3"}[w.in_dtype],
             "data": "synthetic (seeded routing and N(0,1) / N(0,1/k) operands)", "config": config, "roofline": roof}

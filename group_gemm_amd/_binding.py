@@ -13,8 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgroupgemm.so")
 
 GG_DT = {torch.float32: 0, torch.bfloat16: 1, torch.uint8: 2, torch.float8_e4m3fn: 2}
-OP = {"ragged_m": 0, "ragged_k": 1, "padded_m": 2, "padded_k": 3}
-DEV_NEGATIVE_SIZE, DEV_SUM_EXCEEDS_M, DEV_OVER_CAPACITY = 0x1, 0x2, 0x4
+OP = {"ragged_m": 0, "ragged_k": 1, "padded_m": 2, "padded_k": 3, "permute": 4}
+DEV_NEGATIVE_SIZE, DEV_SUM_EXCEEDS_M, DEV_OVER_CAPACITY, DEV_BAD_EXPERT = 0x1, 0x2, 0x4, 0x8
 
 _lib = None
 
@@ -47,6 +47,8 @@ def lib():
                                          vp, vp, i64, vp, sz, vp]
         L.padded_dot.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i32, i64, ctypes.c_int, ctypes.c_int,
                                  vp, vp, vp, sz, vp]
+        L.moe_permute.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i64, i32, ctypes.c_int, vp, sz, vp]
+        L.moe_unpermute.argtypes = [vp, vp, vp, vp, i64, i32, i64, ctypes.c_int, ctypes.c_int, vp]
         L.gg_schedule.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
         L.gg_read_device_status.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
         L.gg_status_string.argtypes = [ctypes.c_int]
@@ -54,7 +56,7 @@ def lib():
         L.gg_abi_version.restype = ctypes.c_int
         for f in ("ragged_dot_m", "ragged_dot_m_nk", "ragged_dot_m_epilogue", "ragged_dot_m_gated", "ragged_dot_k",
                   "ragged_dot_k_epilogue",
-                  "padded_dot", "gg_schedule", "gg_read_device_status"):
+                  "padded_dot", "moe_permute", "moe_unpermute", "gg_schedule", "gg_read_device_status"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -225,6 +227,56 @@ def padded_dot(mode, a, b, group_sizes, capacity, out=None, out_dtype=None, a_sc
     code = lib().padded_dot(OP[op], _p(a), _p(b), _p(group_sizes), _p(out), m, k, n, g, capacity, GG_DT[a.dtype],
                             GG_DT[out.dtype], _p(a_scale), _p(b_scale), _p(ws), ws.numel(), _stream(a.device))
     _check(code, "padded_dot")
+    return out
+
+
+def moe_permute(x, experts, g, x_scale=None, workspace=None, out=None):
+    """Sort the top-k copies of the tokens of x [tokens, k] by expert (experts: int32
+    [tokens, top_k]); returns (sorted_x [M, k], sorted_scale [M, k/32] or None, group_sizes
+    int32 [g], sorted_to_copy int32 [M], copy_to_sorted int32 [M]) with M = tokens * top_k.
+    e4m3 inputs (uint8 codes) need their E8M0 x_scale [tokens, k/32].  `out` may supply
+    that tuple of output tensors (an entry None is allocated)."""
+    tokens, k = x.shape
+    if experts.dim() != 2 or experts.shape[0] != tokens or experts.dtype != torch.int32:
+        raise ValueError("experts must be int32 [tokens, top_k]")
+    top_k = experts.shape[1]
+    M = tokens * top_k
+    dev = x.device
+    sorted_x, sorted_scale, group_sizes, s2c, c2s = out if out is not None else (None,) * 5
+    if sorted_x is None:
+        sorted_x = torch.empty((M, k), dtype=x.dtype, device=dev)
+    if x_scale is not None and sorted_scale is None:
+        sorted_scale = torch.empty((M, x_scale.shape[1]), dtype=torch.uint8, device=dev)
+    if group_sizes is None:
+        group_sizes = torch.empty((g,), dtype=torch.int32, device=dev)
+    if s2c is None:
+        s2c = torch.empty((M,), dtype=torch.int32, device=dev)
+    if c2s is None:
+        c2s = torch.empty((M,), dtype=torch.int32, device=dev)
+    if sorted_x.shape != (M, k) or sorted_x.dtype != x.dtype or group_sizes.shape != (g,) or s2c.shape != (M,) \
+            or c2s.shape != (M,):
+        raise ValueError("output shape/dtype mismatch")
+    ws = _workspace("permute", M, k, 0, g, 0, x.dtype, dev, workspace)
+    code = lib().moe_permute(_p(x), _p(x_scale), _p(experts), _p(sorted_x), _p(sorted_scale), _p(group_sizes), _p(s2c),
+                             _p(c2s), tokens, top_k, k, g, GG_DT[x.dtype], _p(ws), ws.numel(), _stream(dev))
+    _check(code, "moe_permute")
+    return sorted_x, sorted_scale, group_sizes, s2c, c2s
+
+
+def moe_unpermute(y, copy_to_sorted, weights, out=None, out_dtype=torch.bfloat16):
+    """out[t, :] = sum_j weights[t, j] * y[copy_to_sorted[t * top_k + j], :] for y
+    [tokens * top_k, n] in sorted order and fp32 weights [tokens, top_k]."""
+    tokens, top_k = weights.shape
+    M, n = y.shape
+    if M != tokens * top_k or copy_to_sorted.shape != (M,) or copy_to_sorted.dtype != torch.int32:
+        raise ValueError("shape/dtype mismatch")
+    if weights.dtype != torch.float32 or not weights.is_contiguous():
+        raise ValueError("weights must be contiguous float32 [tokens, top_k]")
+    if out is None:
+        out = torch.empty((tokens, n), dtype=out_dtype, device=y.device)
+    code = lib().moe_unpermute(_p(y), _p(copy_to_sorted), _p(weights), _p(out), tokens, top_k, n, GG_DT[y.dtype],
+                               GG_DT[out.dtype], _stream(y.device))
+    _check(code, "moe_unpermute")
     return out
 
 

@@ -11,6 +11,7 @@
 namespace {
 
 constexpr size_t kHeader = 256;   // workspace bytes before any padded buffer (status word first)
+constexpr int64_t kMaxCopies = int64_t(1) << 30;   // moe_permute: tokens * top_k
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -193,6 +194,11 @@ size_t gg_workspace_bytes(gg_op op, int64_t m, int64_t k, int64_t n, int32_t g, 
             const size_t rows = (size_t)g * (size_t)capacity;
             return kHeader + align_up(rows * (size_t)k * elem_bytes(in), 256) + align_up(rows * (size_t)n * elem_bytes(in), 256);
         }
+        case GG_OP_PERMUTE: {
+            if (m > kMaxCopies) return 0;
+            const gg::PermuteGeometry pg = gg::permute_geometry(m);
+            return kHeader + align_up((size_t)pg.nblk * (size_t)g * 4, 256) + align_up((size_t)pg.nblk * 4, 256);
+        }
     }
     return 0;
 }
@@ -358,6 +364,59 @@ gg_status padded_dot(gg_op mode, const void* a, const void* b, const int32_t* gr
     e = gg::launch_pad_scatter(b, pb, group_sizes, (int)m, g, (int)capacity, (long long)n * (long long)es, nullptr, s);
     if (e != hipSuccess) return GG_ERR_HIP;
     return run_k(pa, pb, group_sizes, out, rows, k, n, g, in_dtype, out_dtype, nullptr, (int)capacity, s);
+}
+
+gg_status moe_permute(const void* x, const uint8_t* x_scale, const int32_t* experts, void* sorted_x,
+                      uint8_t* sorted_scale, int32_t* group_sizes, int32_t* sorted_to_copy, int32_t* copy_to_sorted,
+                      int64_t tokens, int32_t top_k, int64_t k, int32_t g, gg_dtype dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    if (!group_sizes || !workspace) return GG_ERR_NULL_PTR;
+    if (tokens < 0 || top_k < 1 || k < 0 || g < 1 || g > GG_MAX_GROUPS || !fits_i32(k)) return GG_ERR_BAD_SHAPE;
+    if (tokens > kMaxCopies / top_k) return GG_ERR_BAD_SHAPE;
+    if (dtype != GG_DT_F32 && dtype != GG_DT_BF16 && dtype != GG_DT_E4M3) return GG_ERR_BAD_DTYPE;
+    const int64_t M = tokens * top_k;
+    if (M > 0 && (!experts || !sorted_to_copy || !copy_to_sorted)) return GG_ERR_NULL_PTR;
+    if (tokens * k > 0 && (!x || !sorted_x)) return GG_ERR_NULL_PTR;
+    const bool mx = dtype == GG_DT_E4M3;
+    if (mx && k % 32 != 0) return GG_ERR_UNSUPPORTED;
+    if (mx && tokens * k > 0 && (!x_scale || !sorted_scale)) return GG_ERR_NULL_PTR;
+    if (!mx && (x_scale || sorted_scale)) return GG_ERR_BAD_DTYPE;
+    const size_t es = elem_bytes(dtype);
+    if (!aligned(x, es) || !aligned(sorted_x, es) || !aligned(experts, 4) || !aligned(group_sizes, 4) ||
+        !aligned(sorted_to_copy, 4) || !aligned(copy_to_sorted, 4) || !aligned(workspace, 16))
+        return GG_ERR_MISALIGNED;
+    if (workspace_bytes < gg_workspace_bytes(GG_OP_PERMUTE, M, k, 0, g, 0, dtype)) return GG_ERR_WORKSPACE_TOO_SMALL;
+    const gg::PermuteGeometry pg = gg::permute_geometry(M);
+    uint8_t* ws = (uint8_t*)workspace;
+    gg::PermuteArgs a{};
+    a.x = x; a.x_scale = mx ? x_scale : nullptr; a.experts = experts;
+    a.sorted_x = sorted_x; a.sorted_scale = mx ? sorted_scale : nullptr;
+    a.group_sizes = group_sizes; a.sorted_to_copy = sorted_to_copy; a.copy_to_sorted = copy_to_sorted;
+    a.status = (uint32_t*)ws;
+    a.total_routed = (int*)(ws + 4);
+    a.counts = (int*)(ws + kHeader);
+    a.bad = (int*)(ws + kHeader + align_up((size_t)pg.nblk * (size_t)g * 4, 256));
+    a.tokens = (int)tokens; a.top_k = top_k; a.g = g;
+    a.row_bytes = k * (int64_t)es;
+    a.scale_row_bytes = mx ? k / 32 : 0;
+    return gg::launch_permute(a, (hipStream_t)stream) == hipSuccess ? GG_OK : GG_ERR_HIP;
+}
+
+gg_status moe_unpermute(const void* y, const int32_t* copy_to_sorted, const float* weights, void* out, int64_t tokens,
+                        int32_t top_k, int64_t n, gg_dtype in_dtype, gg_dtype out_dtype, void* stream) {
+    if (tokens < 0 || top_k < 1 || n < 0 || !fits_i32(n)) return GG_ERR_BAD_SHAPE;
+    if (tokens > 0 && (!copy_to_sorted || !weights)) return GG_ERR_NULL_PTR;
+    if (tokens > kMaxCopies / top_k) return GG_ERR_BAD_SHAPE;
+    if ((in_dtype != GG_DT_F32 && in_dtype != GG_DT_BF16) || (out_dtype != GG_DT_F32 && out_dtype != GG_DT_BF16))
+        return GG_ERR_BAD_DTYPE;
+    if (tokens * n > 0 && (!y || !out)) return GG_ERR_NULL_PTR;
+    if (!aligned(y, elem_bytes(in_dtype)) || !aligned(out, elem_bytes(out_dtype)) || !aligned(copy_to_sorted, 4) ||
+        !aligned(weights, 4))
+        return GG_ERR_MISALIGNED;
+    return gg::launch_combine(y, in_dtype == GG_DT_BF16, (int)(tokens * top_k), copy_to_sorted, weights, (int)tokens,
+                              top_k, (int)n, out, out_dtype == GG_DT_BF16, (hipStream_t)stream) == hipSuccess
+               ? GG_OK
+               : GG_ERR_HIP;
 }
 
 gg_status gg_schedule(const int32_t* group_sizes, int64_t m, int64_t n, int32_t g, int32_t block_m, int32_t block_n,

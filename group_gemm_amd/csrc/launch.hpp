@@ -79,6 +79,30 @@ bool ragged_k_bf16_fast_ok(const KParams& p);
 hipError_t launch_ragged_k_bf16_fast(const KParams& p, int grid, hipStream_t s);
 hipError_t launch_ragged_k_f32(const KParams& p, int grid, hipStream_t s);
 
+// MoE permute / un-permute.
+constexpr int kMaxChunks = 64;   // upper bound on the permute's histogram / rank workgroups
+struct PermuteGeometry { int chunk, nblk; };   // copies per chunk, number of chunks
+PermuteGeometry permute_geometry(int64_t copies);
+struct PermuteArgs {
+    const void* x;                 // [tokens, row_bytes]
+    const void* x_scale;           // [tokens, scale_row_bytes] or NULL
+    const int32_t* experts;        // [tokens * top_k]
+    void* sorted_x;                // [tokens * top_k, row_bytes]
+    void* sorted_scale;            // [tokens * top_k, scale_row_bytes] or NULL
+    int32_t* group_sizes;          // [g]
+    int32_t* sorted_to_copy;       // [tokens * top_k]
+    int32_t* copy_to_sorted;       // [tokens * top_k]
+    int* counts;                   // workspace [nblk, g]
+    int* bad;                      // workspace [nblk]
+    int* total_routed;             // workspace [1]
+    uint32_t* status;
+    int tokens, top_k, g;
+    int64_t row_bytes, scale_row_bytes;
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+hipError_t launch_combine(const void* y, bool y_bf16, int rows, const int32_t* copy_to_sorted, const float* w,
+                          int tokens, int top_k, int n, void* out, bool out_bf16, hipStream_t s);
+
 // Static tile geometry of each family (host-side grid sizing).
 struct TileShape { int bm, bn; };
 TileShape tiles_m_bf16();

@@ -66,12 +66,19 @@ WORKLOADS = {
         # weight tensors, one [8192, 14336] intermediate
         Workload(8, "mixtral8x7b_gated_bf16", "m_gated", "bf16", "bf16", 8192, 4096, 14336, 8,
                  "topk_normal_logits", tokens=4096, top_k=2),
+        # MoE pre/post-processing around the DeepSeek-like routed block: permute 4096 tokens
+        # of width 7168 to their top-8 of 256 experts (m = 32768 copies), and un-permute
+        # [32768, 7168] expert outputs back into 4096 tokens with the router weights
+        Workload(9, "deepseekv3_permute_bf16", "permute", "bf16", "bf16", 32768, 7168, 0, 256,
+                 "rank_zipf_gumbel", tokens=4096, top_k=8),
+        Workload(10, "deepseekv3_unpermute_bf16", "unpermute", "bf16", "bf16", 32768, 0, 7168, 256,
+                 "rank_zipf_gumbel", tokens=4096, top_k=8),
     ]
 }
 
-# the MXFP8 and data-gradient workloads reuse the bf16 forward one's routing stream, so all
-# three see the same sizes
-_ROUTING_WID = {4: 2, 7: 2, 8: 2}
+# the MXFP8, data-gradient and gated workloads reuse the bf16 forward one's routing stream,
+# so all see the same sizes; the permute workloads reuse the DeepSeek-like routing
+_ROUTING_WID = {4: 2, 7: 2, 8: 2, 9: 3, 10: 3}
 
 
 def rng(wid: int, stream: int, seed: int = 0) -> np.random.Generator:
@@ -100,15 +107,16 @@ def topk_indices(scores: np.ndarray, k: int) -> np.ndarray:
     return order[:, :k]
 
 
-def group_sizes(w: Workload, seed: int = 0) -> np.ndarray:
-    """Realised int32[g] group sizes of a workload (host-side, seeded)."""
+_TOPK_ROUTINGS = ("topk_normal_logits", "rank_zipf_gumbel", "rank_zipf_gumbel_zeros")
+
+
+def routing_experts(w: Workload, seed: int = 0) -> np.ndarray:
+    """int32 [tokens, top_k]: the experts the router picks for every token (top-k
+    routings only), the draws group_sizes() counts."""
     r = rng(_ROUTING_WID.get(w.wid, w.wid), 0, seed)
-    if w.routing == "fixed":
-        gs = np.array([16, 0, 40, 8], dtype=np.int32)
-    elif w.routing == "topk_normal_logits":
+    if w.routing == "topk_normal_logits":
         logits = r.standard_normal((w.tokens, w.g))
         experts = topk_indices(logits, w.top_k)
-        gs = np.bincount(experts.ravel(), minlength=w.g).astype(np.int32)
     elif w.routing in ("rank_zipf_gumbel", "rank_zipf_gumbel_zeros"):
         rank = r.permutation(w.g) + 1                      # popularity rank of each expert
         p = rank.astype(np.float64) ** -1.1                # Zipf(s = 1.1) over ranks
@@ -119,7 +127,26 @@ def group_sizes(w: Workload, seed: int = 0) -> np.ndarray:
             logp = np.log(p)
         gumbel = r.gumbel(size=(w.tokens, w.g))
         experts = topk_indices(logp[None, :] + gumbel, w.top_k)   # k distinct experts ~ p
-        gs = np.bincount(experts.ravel(), minlength=w.g).astype(np.int32)
+    else:
+        raise ValueError(f"{w.routing} draws no per-token experts")
+    return np.ascontiguousarray(experts, dtype=np.int32)
+
+
+def router_weights(w: Workload, seed: int = 0) -> np.ndarray:
+    """float32 [tokens, top_k] combine weights: a softmax over N(0,1) scores of the
+    selected experts (positive, each token's weights sum to 1)."""
+    s = rng(w.wid, 3, seed).standard_normal((w.tokens, w.top_k))
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def group_sizes(w: Workload, seed: int = 0) -> np.ndarray:
+    """Realised int32[g] group sizes of a workload (host-side, seeded)."""
+    r = rng(_ROUTING_WID.get(w.wid, w.wid), 0, seed)
+    if w.routing == "fixed":
+        gs = np.array([16, 0, 40, 8], dtype=np.int32)
+    elif w.routing in _TOPK_ROUTINGS:
+        gs = np.bincount(routing_experts(w, seed).ravel(), minlength=w.g).astype(np.int32)
     elif w.routing == "dirichlet_multinomial":
         p = r.dirichlet(np.full(w.g, 0.5))
         gs = r.multinomial(w.tokens * w.top_k, p).astype(np.int32)
@@ -182,7 +209,9 @@ def _uniform(shape, wid, stream, seed, device):
 def make_inputs(w: Workload, device="cpu", seed: int = 0, gs: np.ndarray | None = None):
     """Operands of a workload as torch tensors on ``device``.
 
-    Returns a dict with ``group_sizes`` (int32), and for op "m": ``lhs`` [m,k], ``rhs``
+    Returns a dict with ``group_sizes`` (int32), and for op "permute": ``x`` [tokens,k] and
+    ``experts`` int32 [tokens,top_k]; for op "unpermute": ``y`` [m,n] (expert outputs in
+    sorted order), ``experts`` and ``weights`` float32 [tokens,top_k]; for op "m": ``lhs`` [m,k], ``rhs``
     [g,k,n]; for op "m_nk": ``lhs`` [m,k], ``rhs`` [g,n,k] (k contiguous); for op "k":
     ``lhs`` [m,k], ``dout`` [m,n].  bf16 operands are torch.bfloat16;
     MXFP8 operands are uint8 e4m3 codes plus ``lhs_scale`` [m,k/32] and ``rhs_scale``
@@ -191,7 +220,14 @@ def make_inputs(w: Workload, device="cpu", seed: int = 0, gs: np.ndarray | None 
         gs = group_sizes(w, seed)
     out = {"group_sizes": torch.from_numpy(np.ascontiguousarray(gs, dtype=np.int32)).to(device)}
     m, k, n, g = w.m, w.k, w.n, w.g
-    if w.in_dtype == "f32":
+    if w.op == "permute":
+        out["x"] = _randn((w.tokens, k), w.wid, 1, seed, device).to(torch.bfloat16)
+        out["experts"] = torch.from_numpy(routing_experts(w, seed)).to(device)
+    elif w.op == "unpermute":
+        out["y"] = _randn((m, n), w.wid, 1, seed, device).to(torch.bfloat16)
+        out["experts"] = torch.from_numpy(routing_experts(w, seed)).to(device)
+        out["weights"] = torch.from_numpy(router_weights(w, seed)).to(device)
+    elif w.in_dtype == "f32":
         out["lhs"] = _uniform((m, k), w.wid, 1, seed, device)
         out["rhs"] = _uniform((g, k, n), w.wid, 2, seed, device)
     elif w.op == "k":

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define GG_ABI_VERSION 4
+#define GG_ABI_VERSION 5
 
 typedef enum {
     GG_OK = 0,
@@ -63,7 +63,8 @@ typedef enum {
     GG_OP_RAGGED_M = 0,            /* ragged_dot_m                                          */
     GG_OP_RAGGED_K = 1,            /* ragged_dot_k                                          */
     GG_OP_PADDED_M = 2,            /* padded_dot, non-contracting form                      */
-    GG_OP_PADDED_K = 3             /* padded_dot, contracting form                          */
+    GG_OP_PADDED_K = 3,            /* padded_dot, contracting form                          */
+    GG_OP_PERMUTE = 4              /* moe_permute (m = tokens * top_k copies)               */
 } gg_op;
 
 typedef enum {
@@ -75,6 +76,7 @@ typedef enum {
 #define GG_DEV_NEGATIVE_SIZE 0x1u  /* some group_sizes[h] < 0 (treated as 0)               */
 #define GG_DEV_SUM_EXCEEDS_M 0x2u  /* sum(group_sizes) > m (groups cut off at row m)       */
 #define GG_DEV_OVER_CAPACITY 0x4u  /* padded_dot: a group had more rows than `capacity`    */
+#define GG_DEV_BAD_EXPERT    0x8u  /* moe_permute: an expert id outside [0, g) (not routed)  */
 
 /* Largest group count any call accepts. */
 #define GG_MAX_GROUPS 1024
@@ -188,6 +190,50 @@ gg_status padded_dot(gg_op mode, const void* a, const void* b, const int32_t* gr
                      gg_dtype in_dtype, gg_dtype out_dtype, const uint8_t* a_scale,
                      const uint8_t* b_scale, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/* moe_permute -- the MoE pre-processing that feeds ragged_dot_m: sort the tokens' top-k
+ * copies by expert, gather their rows, and count the rows of every expert.
+ * ("Group-GEMM in XLA", Part 4 "The Three MoE Compute Paths in MaxText", Path 1: repeat
+ * each token top_k times, argsort the flattened expert ids, sort the activations with that
+ * order, bincount the ids into group_sizes.)  M = tokens * top_k copies; copy i is token
+ * i / top_k routed to experts[i].
+ *   x              [tokens, k]      dtype (fp32, bf16 or e4m3)
+ *   x_scale        [tokens, k/32]   E8M0 bytes, e4m3 only (k % 32 == 0), else NULL
+ *   experts        [tokens, top_k]  int32 expert ids; an id outside [0, g) is not routed
+ *                                   (that copy gets no row) and sets GG_DEV_BAD_EXPERT
+ *   sorted_x       [M, k]           dtype: the routed copies' rows grouped by expert, equal
+ *                                   ids in copy order (a stable sort); rows past the routed
+ *                                   total are zero
+ *   sorted_scale   [M, k/32]        e4m3 only, else NULL: the scale rows in the same order
+ *   group_sizes    [g]   int32      rows per expert (the bincount); sums to the routed total
+ *   sorted_to_copy [M]   int32      copy index of each sorted row (the pages' argsort
+ *                                   result), -1 past the routed total
+ *   copy_to_sorted [M]   int32      sorted row of each copy (the inverse order), -1 if the
+ *                                   copy was not routed
+ * Every output element is written on every call; with tokens == 0 only group_sizes (zeros)
+ * is written and the other pointers may be NULL.  All computed on the device (histogram,
+ * scan, rank, gather); nothing is read back.  tokens * top_k <= 2^30.  Workspace:
+ * gg_workspace_bytes(GG_OP_PERMUTE, tokens * top_k, k, 0, g, 0, dtype) bytes, 16-byte
+ * aligned; its status word is rewritten by every call. */
+gg_status moe_permute(const void* x, const uint8_t* x_scale, const int32_t* experts, void* sorted_x,
+                      uint8_t* sorted_scale, int32_t* group_sizes, int32_t* sorted_to_copy,
+                      int32_t* copy_to_sorted, int64_t tokens, int32_t top_k, int64_t k, int32_t g,
+                      gg_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_unpermute -- the MoE post-processing: bring the expert outputs back to token order and
+ * sum each token's top-k rows weighted by the router weights.
+ * ("Group-GEMM in XLA", Part 4 "The Three MoE Compute Paths in MaxText", Path 1: un-sort
+ * with the inverse order, reshape to [tokens, top_k, n], weighted sum over top_k.)
+ *   y              [tokens * top_k, n]  in_dtype (fp32 or bf16): rows in sorted order
+ *   copy_to_sorted [tokens * top_k]     int32, as written by moe_permute; an entry outside
+ *                                       [0, tokens * top_k) (-1: not routed) adds nothing
+ *   weights        [tokens, top_k]      fp32 router weights
+ *   out            [tokens, n]          out_dtype (fp32 or bf16):
+ *     out[t, :] = sum_j weights[t, j] * y[copy_to_sorted[t * top_k + j], :]
+ * fp32 accumulation in j order, one rounding.  No workspace. */
+gg_status moe_unpermute(const void* y, const int32_t* copy_to_sorted, const float* weights, void* out,
+                        int64_t tokens, int32_t top_k, int64_t n, gg_dtype in_dtype,
+                        gg_dtype out_dtype, void* stream);
 
 /* gg_schedule -- runs only the group_sizes -> offsets scan that opens every launch, and
  * writes its tables, so the scan can be tested on its own.

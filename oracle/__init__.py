@@ -7,7 +7,8 @@ numpy arrays into it and adds the padded-dot procedure, written with numpy in fp
 
 Sources: "Group-GEMM in XLA: Making Mixture-of-Experts Fast and Memory-Efficient"
 (AMD ROCm blog) -- Part 1 "The Ragged-Dot Operation" and "The Naive Support, and Why It
-Hurts: Padded-Dot"; Part 3 "Non-Contracting (the MoE Case)" and "Contracting".
+Hurts: Padded-Dot"; Part 3 "Non-Contracting (the MoE Case)" and "Contracting"; Part 4
+"The Three MoE Compute Paths in MaxText" (permute / un-permute, in numpy).
 """
 import ctypes
 import os
@@ -241,6 +242,70 @@ def padded_dot_m(lhs, rhs, group_sizes, capacity, lhs_scale=None, rhs_scale=None
         c = min(s, capacity)
         out[st:st + c] = Q[h, :c]
     return out
+
+
+def bf16_values(a):
+    """fp64 values of bfloat16 bit patterns (uint16): a bfloat16 is the upper half of an
+    IEEE binary32, so the pattern shifted up 16 bits is that binary32 exactly."""
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):   # signalling-NaN patterns stay NaN
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def moe_permute(x, experts, g, x_scale=None):
+    """The MoE pre-processing of the sparse path ("Group-GEMM in XLA", Part 4 "The Three MoE
+    Compute Paths in MaxText", Path 1, permute; and "Router to expert and back"): every
+    token is repeated top_k times (copy i is token i // top_k), the copies are ordered by
+    a stable argsort of the flattened expert ids, the repeated rows are taken in that
+    order, and a bincount of the ids gives group_sizes.
+
+    Reading for ids outside [0, g): such a copy is not routed -- it sorts after every
+    routed copy, gets no row (sorted rows past the routed total are zero, their index -1)
+    and is not counted.  Rows are moved as raw elements (any dtype); `x_scale` rows (the
+    E8M0 scales of e4m3 rows) are moved the same way.
+
+    Returns (sorted_x [M, k], sorted_scale or None, group_sizes int32 [g],
+    sorted_to_copy int32 [M], copy_to_sorted int32 [M]), M = tokens * top_k."""
+    experts = np.asarray(experts)
+    T, K = experts.shape
+    M = T * K
+    flat = experts.reshape(-1).astype(np.int64)
+    routed = (flat >= 0) & (flat < g)
+    order = np.argsort(np.where(routed, flat, g), kind="stable")
+    S = int(routed.sum())
+    sorted_to_copy = np.full(M, -1, dtype=np.int32)
+    sorted_to_copy[:S] = order[:S]
+    copy_to_sorted = np.full(M, -1, dtype=np.int32)
+    copy_to_sorted[order[:S]] = np.arange(S, dtype=np.int32)
+    group_sizes = np.bincount(flat[routed], minlength=g).astype(np.int32)
+
+    def take(a):
+        replicated = np.repeat(np.asarray(a), K, axis=0)
+        out = np.zeros_like(replicated)
+        out[:S] = replicated[order[:S]]
+        return out
+
+    return (take(x), None if x_scale is None else take(x_scale), group_sizes, sorted_to_copy,
+            copy_to_sorted)
+
+
+def moe_unpermute(y, copy_to_sorted, weights):
+    """The MoE post-processing of the sparse path (same page and section, un-permute):
+    the expert outputs y [M, n] (sorted order) are put back in copy order with the inverse
+    permutation, viewed as [tokens, top_k, n], and summed over top_k with the router
+    weights [tokens, top_k], in fp64.  A copy whose entry lies outside [0, M) (-1: not
+    routed) adds nothing.  y is float32 or bfloat16 bit patterns (uint16)."""
+    y = np.asarray(y)
+    yv = bf16_values(y) if y.dtype == np.uint16 else y.astype(np.float64)
+    w = np.asarray(weights, dtype=np.float64)
+    T, K = w.shape
+    M, n = yv.shape
+    assert M == T * K
+    c2s = np.asarray(copy_to_sorted, dtype=np.int64)
+    ok = (c2s >= 0) & (c2s < M)
+    unsorted = np.zeros((M, n))
+    unsorted[ok] = yv[c2s[ok]]
+    return np.einsum("tkn,tk->tn", unsorted.reshape(T, K, n), w)
 
 
 def num_threads():

@@ -23,7 +23,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for required in ("ragged_dot_m", "ragged_dot_m_nk", "ragged_dot_m_epilogue", "ragged_dot_k_epilogue", "ragged_dot_m_gated",
-                     "ragged_dot_k",
+                     "ragged_dot_k", "moe_permute", "moe_unpermute",
                      "padded_dot", "gg_workspace_bytes", "gg_schedule",
                      "gg_read_device_status", "gg_status_string", "gg_abi_version"):
         assert required in names
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert B.abi_version() == 4
+    assert B.abi_version() == 5
     for code in range(8):
         assert B.status_string(code)
 
@@ -145,3 +145,45 @@ def test_schedule_host_validation():
     L = B.lib()
     assert L.gg_schedule(P, 9, 1, 3, 0, 1, P, P, P, None) == 2
     assert L.gg_schedule(NULL, 9, 1, 3, 3, 1, P, P, P, None) == 1
+
+
+def test_permute_host_validation():
+    L = B.lib()
+    need = B.workspace_bytes("permute", 64 * 2, 64, 0, 8)
+    def pm(x=P, xs=NULL, e=P, sx=P, ss=NULL, gs=P, s2c=P, c2s=P, tokens=64, top_k=2, k=64, g=8, dt=1, ws=P, wsb=need):
+        return L.moe_permute(x, xs, e, sx, ss, gs, s2c, c2s, tokens, top_k, k, g, dt, ws, wsb, None)
+    assert pm(e=NULL) == 1
+    assert pm(c2s=NULL) == 1
+    assert pm(ws=NULL) == 1
+    assert pm(x=NULL) == 1
+    assert pm(top_k=0) == 2
+    assert pm(g=0) == 2 and pm(g=1025) == 2
+    assert pm(tokens=-1) == 2
+    assert pm(tokens=1 << 29, top_k=4) == 2      # more than 2^30 copies
+    assert pm(dt=5) == 3
+    assert pm(xs=P) == 3                         # scales only with e4m3
+    assert pm(dt=2) == 1                         # e4m3 without scales
+    assert pm(dt=2, k=48, xs=P, ss=P) == 6       # e4m3 needs k % 32 == 0
+    assert pm(e=ctypes.c_void_p(0x10002)) == 4
+    assert pm(x=ctypes.c_void_p(0x10001)) == 4   # bf16 rows on an odd address
+    assert pm(ws=ctypes.c_void_p(0x10008)) == 4
+    assert pm(wsb=need - 1) == 5
+
+
+def test_unpermute_host_validation():
+    L = B.lib()
+    def up(y=P, c2s=P, w=P, out=P, tokens=64, top_k=2, n=64, ind=1, outd=1):
+        return L.moe_unpermute(y, c2s, w, out, tokens, top_k, n, ind, outd, None)
+    assert up(c2s=NULL) == 1 and up(w=NULL) == 1 and up(y=NULL) == 1
+    assert up(tokens=-1) == 2
+    assert up(top_k=0) == 2 and up(n=-1) == 2
+    assert up(ind=2) == 3 and up(outd=2) == 3
+    assert up(w=ctypes.c_void_p(0x10002)) == 4
+
+
+def test_permute_workspace_size():
+    # header + counts [chunks, g] + one flag per chunk; chunks of at least 1024 copies, at most 64
+    assert B.workspace_bytes("permute", 32768, 7168, 0, 256) == 256 + 32 * 256 * 4 + 256
+    assert B.workspace_bytes("permute", 0, 7168, 0, 256) == 256
+    assert B.workspace_bytes("permute", 1 << 24, 16, 0, 1024) == 256 + 64 * 1024 * 4 + 256
+    assert B.workspace_bytes("permute", (1 << 30) + 1, 16, 0, 8) == 0

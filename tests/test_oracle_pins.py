@@ -461,3 +461,117 @@ def test_row_selection_matches_full_result():
     full = oracle.ragged_dot_m(lhs, rhs, gs)
     rows = np.array([16, 0, 14, 3, 11])
     np.testing.assert_array_equal(oracle.ragged_dot_m(lhs, rhs, gs, rows=rows), full[rows])
+
+
+# ---------------------------------------------------------------------------------------
+# permute / un-permute ("Group-GEMM in XLA", Part 4 "The Three MoE Compute Paths in MaxText")
+
+
+def _brute_permute(experts, g):
+    """Counting loops: for each expert in turn, its copies in index order."""
+    flat = [int(e) for e in np.asarray(experts).reshape(-1)]
+    s2c = []
+    for e in range(g):
+        for i, x in enumerate(flat):
+            if x == e:
+                s2c.append(i)
+    sizes = [sum(1 for x in flat if x == e) for e in range(g)]
+    return s2c, sizes
+
+
+@pytest.mark.parametrize("g,top_k,tokens,bad", [(4, 2, 9, False), (5, 3, 7, True), (1, 1, 5, False),
+                                                (16, 4, 11, True)])
+def test_permute_brute_force(g, top_k, tokens, bad):
+    r = np.random.default_rng([g, top_k, tokens])
+    experts = r.integers(0, g, size=(tokens, top_k)).astype(np.int32)
+    if bad:
+        experts[0, 0] = g          # one past the last expert
+        experts[-1, -1] = -1
+    x = r.standard_normal((tokens, 6)).astype(np.float32)
+    sx, ss, gs, s2c, c2s = oracle.moe_permute(x, experts, g)
+    want_s2c, want_gs = _brute_permute(experts, g)
+    S = len(want_s2c)
+    M = tokens * top_k
+    assert ss is None
+    assert gs.tolist() == want_gs
+    assert s2c[:S].tolist() == want_s2c and (s2c[S:] == -1).all()
+    for p, i in enumerate(want_s2c):
+        assert np.array_equal(sx[p], x[i // top_k])
+        assert c2s[i] == p
+    assert (sx[S:] == 0).all()
+    routed = set(want_s2c)
+    assert all(c2s[i] == -1 for i in range(M) if i not in routed)
+
+
+def test_permute_worked_example():
+    """Worked by hand: three tokens, top-2 of three experts, ids [[2, 0], [1, 2], [0, 0]]
+    flatten to [2, 0, 1, 2, 0, 0]; the stable argsort is [1, 4, 5, 2, 0, 3], the bincount
+    [3, 1, 2] and the inverse order [4, 0, 3, 5, 1, 2]."""
+    x = np.array([[10.0], [20.0], [30.0]], dtype=np.float32)
+    sx, _, gs, s2c, c2s = oracle.moe_permute(x, np.array([[2, 0], [1, 2], [0, 0]], np.int32), 3)
+    assert s2c.tolist() == [1, 4, 5, 2, 0, 3]
+    assert gs.tolist() == [3, 1, 2]
+    assert sx[:, 0].tolist() == [10.0, 30.0, 30.0, 20.0, 10.0, 20.0]
+    assert c2s.tolist() == [4, 0, 3, 5, 1, 2]
+
+
+def test_unpermute_of_permuted_rows_is_weighted_identity():
+    """With the expert block replaced by the identity, un-permute(permute(x)) is
+    x[t] * (sum of the weights of t's routed copies)."""
+    r = np.random.default_rng(7)
+    T, K, g, k = 40, 3, 6, 10
+    experts = r.integers(0, g, size=(T, K)).astype(np.int32)
+    experts[3, 1] = -1                      # an unrouted copy adds nothing
+    w = r.random((T, K)).astype(np.float32)
+    x = r.standard_normal((T, k)).astype(np.float32)
+    sx, _, _, _, c2s = oracle.moe_permute(x, experts, g)
+    out = oracle.moe_unpermute(sx, c2s, w)
+    wsum = np.where(experts >= 0, w.astype(np.float64), 0.0).sum(axis=1)
+    np.testing.assert_allclose(out, x.astype(np.float64) * wsum[:, None], rtol=1e-15, atol=0)
+
+
+def test_unpermute_brute_force_bf16():
+    r = np.random.default_rng(8)
+    T, K, n = 5, 2, 7
+    y = _bf16_bits(r.standard_normal((T * K, n)))
+    c2s = r.permutation(T * K).astype(np.int32)
+    c2s[4] = -1
+    w = r.random((T, K)).astype(np.float32)
+    yv = _bf16_values(y)
+    want = np.zeros((T, n))
+    for t in range(T):
+        for j in range(K):
+            p = c2s[t * K + j]
+            if p >= 0:
+                want[t] += float(w[t, j]) * yv[p]
+    np.testing.assert_allclose(oracle.moe_unpermute(y, c2s, w), want, rtol=1e-15, atol=0)
+
+
+def test_sparse_path_equals_dense_path():
+    """Path 1 (permute, ragged dot, un-permute) computes the same layer output as Path 2
+    (every token through every expert, combined with weights that are zero off the
+    token's selection) -- the pages' comparison of the two dropless paths."""
+    r = np.random.default_rng(9)
+    T, K, g, k, n = 24, 2, 5, 16, 12
+    logits = r.standard_normal((T, g))
+    experts = W.topk_indices(logits, K).astype(np.int32)
+    w = r.random((T, K)).astype(np.float32)
+    x = r.standard_normal((T, k)).astype(np.float32)
+    wts = r.standard_normal((g, k, n)).astype(np.float32)
+    sx, _, gs, _, c2s = oracle.moe_permute(x, experts, g)
+    y = oracle.ragged_dot_m(sx, wts, gs)
+    sparse = oracle.moe_unpermute(y.astype(np.float32), c2s, w)
+    dense_w = np.zeros((T, g))
+    for t in range(T):
+        for j in range(K):
+            dense_w[t, experts[t, j]] += w[t, j]
+    per_expert = np.einsum("tk,ekn->ten", x.astype(np.float64), wts.astype(np.float64))
+    dense = np.einsum("ten,te->tn", per_expert, dense_w)
+    np.testing.assert_allclose(sparse, dense, rtol=1e-6, atol=1e-6)   # y rounded to fp32 once
+
+
+def test_bf16_values_match_library():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    a, b = oracle.bf16_values(bits), _bf16_values(bits)
+    same = (a == b) | (np.isnan(a) & np.isnan(b))
+    assert same.all()
