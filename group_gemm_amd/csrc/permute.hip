@@ -69,7 +69,19 @@ __global__ __launch_bounds__(NT) void rank(const int32_t* __restrict__ experts, 
     // 1. start of this chunk's copies of expert e
     int total = 0, before = 0;
     if (t < g) {
-        for (int b = 0; b < nblk; ++b) {
+        // eight chunks' counts in flight at a time (they come from other CUs' caches)
+        int b = 0;
+        for (; b + 8 <= nblk; b += 8) {
+            int x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = counts[(size_t)(b + u) * g + t];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                total += x[u];
+                before += b + u < c ? x[u] : 0;
+            }
+        }
+        for (; b < nblk; ++b) {
             const int x = counts[(size_t)b * g + t];
             total += x;
             before += b < c ? x : 0;
