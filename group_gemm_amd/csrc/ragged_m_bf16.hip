@@ -222,46 +222,62 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-        // One half slice: the MFMAs on `cur` with, after each, at most one ring load (of
-        // slice `stage`, when DMA) and one fragment read of `nxt` (k step s of slot a / b).
-        // The order is pinned so the loads and reads issue while the MFMAs run.
-        auto phase = [&](auto nb_c, auto dma_c, Frags<MI, NJ>& cur, Frags<MI, NJ>& nxt, const uint16_t* a,
+        // One half slice: the MFMAs on `cur` with, after some, one ring load of slice `stage`
+        // and, after each, at most one fragment read of `nxt` (k step s of slot a / b).  HALF
+        // selects the ring loads: 0 none, 1 the first PER / 2 (the A blocks), 2 the rest; they
+        // are spread evenly over the MFMAs, so the four waves' loads reach the memory pipeline
+        // one at a time rather than in a burst.  The order is pinned so the loads and reads
+        // issue while the MFMAs run.
+        auto phase = [&](auto nb_c, auto half_c, Frags<MI, NJ>& cur, Frags<MI, NJ>& nxt, const uint16_t* a,
                          const uint16_t* b, int s, int stage) {
             constexpr int NB = decltype(nb_c)::value;
-            constexpr bool DMA = decltype(dma_c)::value;
-            constexpr int NM = NB * NJ, NR = NB > 0 ? NB + NJ : 0, ND = DMA ? C::PER : 0;
-            constexpr int NOPS = NM > NR ? (NM > ND ? NM : ND) : (NR > ND ? NR : ND);
+            constexpr int HALF = decltype(half_c)::value;
+            constexpr int NM = NB * NJ, NR = NB > 0 ? NB + NJ : 0, ND = HALF ? C::PER / 2 : 0;
+            constexpr int SP = ND > 0 && NM >= ND ? NM / ND : 1;   // MFMAs between two ring loads
+            constexpr int LD = ND > 0 ? (ND - 1) * SP + 1 : 0;
+            constexpr int NOPS = NM > NR ? (NM > LD ? NM : LD) : (NR > LD ? NR : LD);
             static_for<0, NOPS>([&](auto o_c) {
                 constexpr int o = decltype(o_c)::value;
                 if constexpr (o < NM) {   // column block major: block (o % NB, o / NB)
                     constexpr int i = o % (NB > 0 ? NB : 1), j = o / (NB > 0 ? NB : 1);
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
                 }
-                if constexpr (o < ND) dma_one(o_c, stage);
+                if constexpr (ND > 0 && o % SP == 0 && o / SP < ND)
+                    dma_one(std::integral_constant<int, (HALF - 1) * (C::PER / 2) + o / SP>{}, stage);
                 if constexpr (o < NR) read_one<MI, NJ, NB, o, B_NK>(nxt, a, b, s, r0w, c0w);
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
 
+        // Slice s is loaded in two halves: the first in the second half slice of iteration
+        // s - 4 (its slot, read last in the first half slice of that iteration, is free once
+        // the iteration's barrier has passed), the second in the first half slice of
+        // iteration s - 3.  Either way PER * (STAGES - 2) loads are issued after slice kt + 1's
+        // last one by the time iteration kt waits for it.
+        static_assert(STAGES == 4 && C::PER % 2 == 0, "the split ring loads assume a 4-slot ring");
         auto run = [&](auto nb_c) {
             constexpr int NB = decltype(nb_c)::value;
+            constexpr std::integral_constant<int, 0> none{};
+            constexpr std::integral_constant<int, 1> first{};
+            constexpr std::integral_constant<int, 2> second{};
             Frags<MI, NJ> f0, f1;
             static_for<0, STAGES - 1>([&](auto st_c) { static_for<0, C::PER>([&](auto d_c) { dma_one(d_c, decltype(st_c)::value); }); });
+            static_for<0, C::PER / 2>([&](auto d_c) { dma_one(d_c, STAGES - 1); });
             // slice 0 in LDS.  Loads complete in issue order among themselves; output stores of
             // the previous tile still in flight only raise the count, so this can only wait longer.
-            wait_vm<C::PER * (STAGES - 2)>();
+            wait_vm<C::PER * (STAGES - 2) + C::PER / 2>();
             lds_barrier();
             if constexpr (NB > 0)
                 static_for<0, NB + NJ>([&](auto r_c) { read_one<MI, NJ, NB, decltype(r_c)::value, B_NK>(f0, sm.ring.a[0], sm.ring.b[0], 0, r0w, c0w); });
             for (int kt = 0; kt + 1 < nk; ++kt) {
                 const int slot = kt % STAGES, ns = (kt + 1) % STAGES;
-                phase(nb_c, std::true_type{}, f0, f1, sm.ring.a[slot], sm.ring.b[slot], 1, kt + STAGES - 1);
+                phase(nb_c, second, f0, f1, sm.ring.a[slot], sm.ring.b[slot], 1, kt + STAGES - 1);
                 wait_vm<C::PER * (STAGES - 2)>();   // slice kt + 1 in LDS
                 lds_barrier();
-                phase(nb_c, std::false_type{}, f1, f0, sm.ring.a[ns], sm.ring.b[ns], 0, 0);
+                phase(nb_c, first, f1, f0, sm.ring.a[ns], sm.ring.b[ns], 0, kt + STAGES);
             }
             const int last = (nk - 1) % STAGES;
-            phase(nb_c, std::false_type{}, f0, f1, sm.ring.a[last], sm.ring.b[last], 1, 0);
+            phase(nb_c, none, f0, f1, sm.ring.a[last], sm.ring.b[last], 1, 0);
             mma<MI, NJ, NB>(f1, acc);
         };
         if (nk > 0) with_nb<MI>(nb, run);
