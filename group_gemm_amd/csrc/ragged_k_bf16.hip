@@ -169,39 +169,48 @@ __global__ __launch_bounds__(NT, 1) void kernel(KParams p) {
 
         // one half slice: MFMAs on `cur`, each followed by at most one ring load and one
         // fragment read of `nxt` (step s of slot a / b), in a pinned order
-        auto phase = [&](auto nb_c, auto dma_c, Frags& cur, Frags& nxt, const uint16_t* a, const uint16_t* b, int s,
+        auto phase = [&](auto nb_c, auto half_c, Frags& cur, Frags& nxt, const uint16_t* a, const uint16_t* b, int s,
                          int stage) {
             constexpr int NB = decltype(nb_c)::value;
-            constexpr bool DMA = decltype(dma_c)::value;
-            constexpr int NM = NB * NJ, NR = NB > 0 ? NB + NJ : 0, ND = DMA ? PER : 0;
-            constexpr int NOPS = NM > NR ? (NM > ND ? NM : ND) : (NR > ND ? NR : ND);
+            constexpr int HALF = decltype(half_c)::value;   // ring loads: 0 none, 1 the first PER / 2, 2 the rest
+            constexpr int NM = NB * NJ, NR = NB > 0 ? NB + NJ : 0, ND = HALF ? PER / 2 : 0;
+            constexpr int SP = ND > 0 && NM >= ND ? NM / ND : 1;   // MFMAs between two ring loads
+            constexpr int LD = ND > 0 ? (ND - 1) * SP + 1 : 0;
+            constexpr int NOPS = NM > NR ? (NM > LD ? NM : LD) : (NR > LD ? NR : LD);
             static_for<0, NOPS>([&](auto o_c) {
                 constexpr int o = decltype(o_c)::value;
                 if constexpr (o < NM) {
                     constexpr int i = o % (NB > 0 ? NB : 1), j = o / (NB > 0 ? NB : 1);
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
                 }
-                if constexpr (o < ND) dma_one(o_c, stage);
+                if constexpr (ND > 0 && o % SP == 0 && o / SP < ND)
+                    dma_one(std::integral_constant<int, (HALF - 1) * (PER / 2) + o / SP>{}, stage);
                 if constexpr (o < NR) read_one<NB, o>(nxt, a, b, s, r0w, c0w);
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
+        static_assert(STAGES == 4 && PER % 2 == 0, "the split ring loads assume a 4-slot ring");
         auto run = [&](auto nb_c) {
             constexpr int NB = decltype(nb_c)::value;
             Frags f0, f1;
+            // slice s is loaded in two halves, spread over the MFMAs: the first in the second
+            // half slice of iteration s - 4 (its slot is free once that iteration's barrier has
+            // passed), the rest in the first half slice of iteration s - 3; either way
+            // PER * (STAGES - 2) loads follow slice kt + 1's last one when iteration kt waits
             static_for<0, STAGES - 1>([&](auto st_c) { static_for<0, PER>([&](auto d_c) { dma_one(d_c, decltype(st_c)::value); }); });
-            wait_vm<PER * (STAGES - 2)>();   // slice 0 in LDS
+            static_for<0, PER / 2>([&](auto d_c) { dma_one(d_c, STAGES - 1); });
+            wait_vm<PER * (STAGES - 2) + PER / 2>();   // slice 0 in LDS
             lds_barrier();
             if constexpr (NB > 0) static_for<0, NB + NJ>([&](auto r_c) { read_one<NB, decltype(r_c)::value>(f0, sm.ring.a[0], sm.ring.b[0], 0, r0w, c0w); });
             for (int kt = 0; kt + 1 < nk; ++kt) {
                 const int slot = kt % STAGES, ns = (kt + 1) % STAGES;
-                phase(nb_c, std::true_type{}, f0, f1, sm.ring.a[slot], sm.ring.b[slot], 1, kt + STAGES - 1);
+                phase(nb_c, std::integral_constant<int, 2>{}, f0, f1, sm.ring.a[slot], sm.ring.b[slot], 1, kt + STAGES - 1);
                 wait_vm<PER * (STAGES - 2)>();   // slice kt + 1 in LDS
                 lds_barrier();
-                phase(nb_c, std::false_type{}, f1, f0, sm.ring.a[ns], sm.ring.b[ns], 0, 0);
+                phase(nb_c, std::integral_constant<int, 1>{}, f1, f0, sm.ring.a[ns], sm.ring.b[ns], 0, kt + STAGES);
             }
             const int last = (nk - 1) % STAGES;
-            phase(nb_c, std::false_type{}, f0, f1, sm.ring.a[last], sm.ring.b[last], 1, 0);
+            phase(nb_c, std::integral_constant<int, 0>{}, f0, f1, sm.ring.a[last], sm.ring.b[last], 1, 0);
             static_for<0, NB * NJ>([&](auto o_c) {   // the last half slice's MFMAs
                 constexpr int o = decltype(o_c)::value, i = o % (NB > 0 ? NB : 1), j = o / (NB > 0 ? NB : 1);
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.b[j], f1.a[i], acc[i][j], 0, 0, 0);

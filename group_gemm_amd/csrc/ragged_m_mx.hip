@@ -198,19 +198,25 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
         auto run = [&](auto nb_c) {
             constexpr int NB = decltype(nb_c)::value;
             Frags f;
+            // Slice s is loaded in two halves: ring loads 0 .. PER/2 - 1 in phase 2 of iteration
+            // s - 4 (its slot, read last in phase 1 of that iteration, is free once the
+            // iteration's barrier has passed), the rest in phase 1 of iteration s - 3, so the
+            // loads are spread over all the slice's MFMAs.  Either way PER * (STAGES - 2)
+            // loads are issued after slice kt + 1's last one by the time iteration kt waits.
             static_for<0, STAGES - 1>([&](auto st_c) { static_for<0, PER>([&](auto d_c) { dma_one(d_c, decltype(st_c)::value); }); });
-            wait_vm<PER * (STAGES - 2)>();   // slice 0 in LDS
+            static_for<0, PER / 2>([&](auto d_c) { dma_one(d_c, STAGES - 1); });
+            wait_vm<PER * (STAGES - 2) + PER / 2>();   // slice 0 in LDS
             lds_barrier();
             if constexpr (NB > 0) {
                 static_for<0, NB>([&](auto i_c) { read_a(f, decltype(i_c)::value, sm.ring[0], r0w, 0); });
                 read_b(f, 0, sm.ring[0], c0w, cp);
                 read_b(f, 1, sm.ring[0], c0w, cp);
             }
-            // phase 1 of slice kt: MFMAs (i, 0..1), ring loads of slice `stage` (when DMA),
-            // reads of B blocks 2, 3 of slot kt
+            // phase 1 of slice kt: MFMAs (i, 0..1), the second half of the ring loads of slice
+            // `stage` (when DMA), reads of B blocks 2, 3 of slot kt
             auto phase1 = [&](auto dma_c, const Slot& s, int stage) {
                 constexpr bool DMA = decltype(dma_c)::value;
-                constexpr int NM = 2 * NB, ND = DMA ? PER : 0, NR = NB > 0 ? 2 : 0;
+                constexpr int NM = 2 * NB, ND = DMA ? PER - PER / 2 : 0, NR = NB > 0 ? 2 : 0;
                 constexpr int NOPS = ND + NR;
                 constexpr int PERM = NM > 0 ? (NOPS + NM - 1) / NM : NOPS;   // ops after each MFMA
                 constexpr int NSLOT = NM > 0 ? NM : 1;
@@ -227,35 +233,44 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
                         else {
                             constexpr int d = o - (NR > 0 ? (o > RB3 ? 2 : (o > RB2 ? 1 : 0)) : 0);
                             static_assert(d >= 0 && d < ND, "op index");
-                            dma_one(std::integral_constant<int, d>{}, stage);
+                            dma_one(std::integral_constant<int, PER / 2 + d>{}, stage);
                         }
                     });
                     __builtin_amdgcn_sched_barrier(0);
                 });
             };
             // phase 2 of slice kt: MFMAs (i, 2..3), reads of slot kt + 1 (A block i after its
-            // last MFMA, B blocks 0, 1 spread over the first MFMAs) when NEXT
-            auto phase2 = [&](auto next_c, const Slot& s, int ks1) {
+            // last MFMA, B blocks 0, 1 spread over the first MFMAs) when NEXT, and the first half
+            // of the ring loads of slice `stage`, spread over the MFMAs
+            auto phase2 = [&](auto next_c, const Slot& s, int ks1, int stage) {
                 constexpr bool NEXT = decltype(next_c)::value;
-                static_for<0, 2 * NB>([&](auto m_c) {
+                constexpr int NM = 2 * NB, ND = NEXT ? PER / 2 : 0;
+                static_for<0, NM>([&](auto m_c) {
                     constexpr int m = decltype(m_c)::value;
                     mfma(f, m >> 1, 2 + (m & 1));
                     if constexpr (NEXT) {
                         if constexpr (m == 0) read_b(f, 0, s, c0w, cp);
                         if constexpr (m == 2 || (NB == 1 && m == 1)) read_b(f, 1, s, c0w, cp);
                         if constexpr (m & 1) read_a(f, m >> 1, s, r0w, ks1);
+                        // ring load q after MFMA q * NM / ND (several after the last when NM < ND)
+                        static_for<0, ND>([&](auto q_c) {
+                            constexpr int q = decltype(q_c)::value;
+                            constexpr int at = q * NM / ND;
+                            if constexpr (at == m) dma_one(q_c, stage);
+                        });
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 });
+                if constexpr (NM == 0 && NEXT) static_for<0, ND>([&](auto q_c) { dma_one(q_c, stage); });
             };
             for (int kt = 0; kt + 1 < nk; ++kt) {
                 phase1(std::true_type{}, sm.ring[kt % STAGES], kt + STAGES - 1);
                 wait_vm<PER * (STAGES - 2)>();   // slice kt + 1 in LDS
                 lds_barrier();
-                phase2(std::true_type{}, sm.ring[(kt + 1) % STAGES], kt + 1);
+                phase2(std::true_type{}, sm.ring[(kt + 1) % STAGES], kt + 1, kt + STAGES);
             }
             phase1(std::false_type{}, sm.ring[(nk - 1) % STAGES], 0);
-            phase2(std::false_type{}, sm.ring[0], 0);
+            phase2(std::false_type{}, sm.ring[0], 0, 0);
         };
         if (nk > 0) with_nb<MI>(nb, run);
         // Every ring load has landed (the zero-fill loads of slices past the end may still be
