@@ -33,6 +33,12 @@ namespace gg {
 namespace perm {
 
 constexpr int NT = 1024;    // threads of the histogram and rank workgroups
+// Cache policy of the row copies' whole-line stores: each sorted row is written once and not
+// read again here, so the stores carry gfx950's nontemporal (`nt`) hint, which lets them
+// stream past the caches (measured +13 % on the permute, +12 % on the un-permute).  The
+// GEMM kernels do not use it: their fp32 tile stores are partial lines per instruction and
+// ran at half speed with it.
+constexpr int kNontemporal = 2;
 constexpr int NW = NT / 64;
 // row kernels (scatter, combine): 256-thread workgroups, WPR waves share one token's row
 constexpr int WPR = 2;
@@ -187,7 +193,7 @@ __device__ inline void copy_row(const uint8_t* __restrict__ src, int64_t rb, con
                 if (p < 0 || p >= M) continue;
                 const ring::rsrc_t rd = ring::make_rsrc(uniform_ptr(dst0 + (size_t)p * rb + o0), len);
 #pragma unroll
-                for (int u = 0; u < 8; ++u) ring::bstore(rd, u * 1024 + 16 * l, v[u]);
+                for (int u = 0; u < 8; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, u * 1024 + 16 * l, 0, kNontemporal);
             }
         }
     } else {
@@ -239,34 +245,36 @@ __global__ __launch_bounds__(256) void scatter(const uint8_t* __restrict__ x, co
 // out[t, :] = sum_j w[t, j] * y[copy_to_sorted[t * top_k + j], :], fp32 sum in j order;
 // entries outside [0, rows) contribute nothing.  WPR waves per token; VEC: 8 consecutive
 // columns per lane with 16-byte (bf16) or 2 x 16-byte (fp32) accesses.
+// (streaming accesses: each expert-output row is read once and each token row written once,
+// so they bypass the caches' retention with nontemporal hints)
 template <typename InT>
 __device__ inline void load8(const InT* p, float (&v)[8]) {
     if constexpr (sizeof(InT) == 2) {
-        const uint4 q = *(const uint4*)p;
-        const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+        const i32x4 q = __builtin_nontemporal_load((const i32x4*)p);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            v[2 * e] = __uint_as_float(u[e] << 16);
-            v[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+            v[2 * e] = __uint_as_float((uint32_t)q[e] << 16);
+            v[2 * e + 1] = __uint_as_float((uint32_t)q[e] & 0xffff0000u);
         }
     } else {
-        const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        const f32x4 a = __builtin_nontemporal_load((const f32x4*)p), b = __builtin_nontemporal_load((const f32x4*)(p + 4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[e] = a[e];
+            v[4 + e] = b[e];
+        }
     }
 }
 template <typename OutT>
 __device__ inline void store8(OutT* p, const float (&v)[8]) {
     if constexpr (sizeof(OutT) == 2) {
-        uint4 q;
-        q.x = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        q.y = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-        q.z = f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-        q.w = f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
-        *(uint4*)p = q;
+        i32x4 q;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = (int)(f32_to_bf16(v[2 * e]) | ((uint32_t)f32_to_bf16(v[2 * e + 1]) << 16));
+        __builtin_nontemporal_store(q, (i32x4*)p);
     } else {
-        *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
-        *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, (f32x4*)p);
+        __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, (f32x4*)(p + 4));
     }
 }
 __device__ inline float ld1(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
