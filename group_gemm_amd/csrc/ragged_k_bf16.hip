@@ -226,9 +226,9 @@ __global__ __launch_bounds__(NT, 1) void kernel(KParams p) {
         const rsrc_t ro = make_rsrc((const char*)p.out + ((size_t)grp * p.k + i0) * p.n * osz, (uint32_t)(rows_valid * p.n * osz));
         static_assert(4 * 32 * (WCOLS + 4) * 4 <= (int)sizeof(sm.ring), "epilogue strips fit the ring");
         const EpiTile ep{nullptr, p.alpha, p.beta};
-        store_acc<MI, NJ, WCOLS, OutT, EPI>(acc, reinterpret_cast<float*>(&sm.ring) + wave * 32 * (WCOLS + 4), ro, p.n, j0, r0w,
-                                            c0w, ep);
-        if constexpr (osz == 2 || EPI) lds_barrier();   // strips read before the next tile's ring loads land there
+        store_acc<MI, NJ, WCOLS, OutT, EPI, true>(acc, reinterpret_cast<float*>(&sm.ring) + wave * 32 * (WCOLS + 4), ro, p.n, j0,
+                                                  r0w, c0w, ep);
+        lds_barrier();   // strips read before the next tile's ring loads land there
     }
     wait_vm<0>();   // no ring load may still be writing LDS when the workgroup ends
 }

@@ -98,81 +98,23 @@ struct EpiTile {
 // Epilogue of one wave's MI x NJ blocks of 32 x 32 fp32 results laid out as
 // acc[i][j][4q + e] = C[r0w + 32i + (lane & 31)][c0w + 32j + 8q + 4h + e], h = lane / 32
 // (the MFMA took the column operand first).  `ro` covers the tile's valid rows of the
-// output; col0 is the tile's first column.  Plain fp32 results are stored straight from
-// AGPRs.  bf16 results, and any result with an epilogue (EPI), go through `strip`, a
-// wave-private 32 x (WCOLS + 4) fp32 area of LDS: the accumulators are written there
-// straight from AGPRs, come back 8 consecutive columns per lane, and leave as 16-byte
-// stores, a whole row segment per WCOLS / 8 lanes (converting or scaling in place would
-// copy every accumulator through VGPRs).  The row pitch WCOLS + 4 floats spreads the 32
-// rows one write touches over all banks.  The caller synchronises the waves before the
-// strip's memory is reused.
-template <int MI, int NJ, int WCOLS, typename OutT, bool EPI>
+// output; col0 is the tile's first column.  With STRIP (always for bf16 results and for an
+// epilogue) results go through `strip`, a wave-private 32 x (WCOLS + 4) fp32 area of LDS:
+// the accumulators are written there straight from AGPRs, come back 8 consecutive columns
+// per lane, are converted or scaled (EPI), and leave as 16-byte stores, a whole row segment
+// per WCOLS / 8 lanes.  Converting or scaling in registers would copy every accumulator
+// through VGPRs.  Without STRIP, fp32 results are stored straight from AGPRs, a quarter
+// cache line per row and instruction: fewer registers, but slower writes (the fp32
+// weight-gradient kernel, whose output dominates its traffic, takes the strip: 12 % faster).
+// The row pitch WCOLS + 4 floats spreads the 32 rows one write touches over all banks.  The
+// caller synchronises the waves before the strip's memory is reused.
+template <int MI, int NJ, int WCOLS, typename OutT, bool EPI, bool STRIP = (sizeof(OutT) == 2 || EPI)>
 __device__ inline void store_acc(const f32x16 (&acc)[MI][NJ], float* strip, rsrc_t ro, int n, int col0, int r0w, int c0w,
                                  const EpiTile& ep) {
     const int l = threadIdx.x & 63, h = l >> 5;
     constexpr bool osz2 = sizeof(OutT) == 2;
-    if constexpr (osz2 || EPI) {
-        constexpr int SP = WCOLS + 4, LPR = WCOLS / 8, RPS = 64 / LPR;
-        const int rr = l / LPR, g = l % LPR;
-        const int col = col0 + c0w + 8 * g;
-        const bool col_ok = col < n;
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    *(f32x4*)(strip + (l & 31) * SP + 32 * j + 8 * q + 4 * h) = v;
-                }
-#pragma unroll
-            for (int t2 = 0; t2 < 32 / RPS; ++t2) {
-                const int rs = t2 * RPS + rr;   // row within the strip
-                const f32x4 lo = *(const f32x4*)(strip + rs * SP + 8 * g);
-                const f32x4 hi = *(const f32x4*)(strip + rs * SP + 8 * g + 4);
-                float x[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                const int r = r0w + 32 * i + rs;
-                const uint32_t off = col_ok ? (uint32_t)(r * n + col) * (uint32_t)sizeof(OutT) : kOOB;
-                if constexpr (EPI) {
-                    float old[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) old[e] = 0.f;
-                    if (ep.beta != 0.f) {   // rows past the tile and columns past n read as 0
-                        if constexpr (osz2) {
-                            const i32x4 c = __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                old[2 * e] = __uint_as_float((uint32_t)c[e] << 16);
-                                old[2 * e + 1] = __uint_as_float((uint32_t)c[e] & 0xffff0000u);
-                            }
-                        } else {
-                            const i32x4 c0 = __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0);
-                            const i32x4 c1 = __builtin_amdgcn_raw_buffer_load_b128(ro, col_ok ? off + 16u : kOOB, 0, 0);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                old[e] = __int_as_float(c0[e]);
-                                old[4 + e] = __int_as_float(c1[e]);
-                            }
-                        }
-                    }
-                    // the bias row is re-read per output row (cached) to keep few registers live
-                    float bias[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) bias[e] = ep.bias_row && col + e < n ? ep.bias_row[col + e] : 0.f;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = ep.alpha * x[e] + bias[e] + ep.beta * old[e];
-                }
-                if constexpr (osz2) {
-                    const i32x4 v = {(int)pack_bf16(x[0], x[1]), (int)pack_bf16(x[2], x[3]), (int)pack_bf16(x[4], x[5]),
-                                     (int)pack_bf16(x[6], x[7])};
-                    bstore(ro, off, v);
-                } else {
-                    bstore(ro, off, i32x4{__float_as_int(x[0]), __float_as_int(x[1]), __float_as_int(x[2]), __float_as_int(x[3])});
-                    bstore(ro, col_ok ? off + 16u : kOOB, i32x4{__float_as_int(x[4]), __float_as_int(x[5]), __float_as_int(x[6]), __float_as_int(x[7])});
-                }
-            }
-        }
-    } else {
+    static_assert(STRIP || !(osz2 || EPI), "bf16 results and epilogues go through the strip");
+    if constexpr (!STRIP) {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -185,6 +127,67 @@ __device__ inline void store_acc(const f32x16 (&acc)[MI][NJ], float* strip, rsrc
                                      __float_as_int(acc[i][j][4 * q + 2]), __float_as_int(acc[i][j][4 * q + 3])};
                     bstore(ro, col < n ? (uint32_t)(r * n + col) * 4u : kOOB, v);
                 }
+        return;
+    }
+    constexpr int SP = WCOLS + 4, LPR = WCOLS / 8, RPS = 64 / LPR;
+    const int rr = l / LPR, g = l % LPR;
+    const int col = col0 + c0w + 8 * g;
+    const bool col_ok = col < n;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                *(f32x4*)(strip + (l & 31) * SP + 32 * j + 8 * q + 4 * h) = v;
+            }
+#pragma unroll
+        for (int t2 = 0; t2 < 32 / RPS; ++t2) {
+            const int rs = t2 * RPS + rr;   // row within the strip
+            const f32x4 lo = *(const f32x4*)(strip + rs * SP + 8 * g);
+            const f32x4 hi = *(const f32x4*)(strip + rs * SP + 8 * g + 4);
+            float x[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const int r = r0w + 32 * i + rs;
+            const uint32_t off = col_ok ? (uint32_t)(r * n + col) * (uint32_t)sizeof(OutT) : kOOB;
+            if constexpr (EPI) {
+                float old[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) old[e] = 0.f;
+                if (ep.beta != 0.f) {   // rows past the tile and columns past n read as 0
+                    if constexpr (osz2) {
+                        const i32x4 c = __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            old[2 * e] = __uint_as_float((uint32_t)c[e] << 16);
+                            old[2 * e + 1] = __uint_as_float((uint32_t)c[e] & 0xffff0000u);
+                        }
+                    } else {
+                        const i32x4 c0 = __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0);
+                        const i32x4 c1 = __builtin_amdgcn_raw_buffer_load_b128(ro, col_ok ? off + 16u : kOOB, 0, 0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            old[e] = __int_as_float(c0[e]);
+                            old[4 + e] = __int_as_float(c1[e]);
+                        }
+                    }
+                }
+                // the bias row is re-read per output row (cached) to keep few registers live
+                float bias[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bias[e] = ep.bias_row && col + e < n ? ep.bias_row[col + e] : 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = ep.alpha * x[e] + bias[e] + ep.beta * old[e];
+            }
+            if constexpr (osz2) {
+                const i32x4 v = {(int)pack_bf16(x[0], x[1]), (int)pack_bf16(x[2], x[3]), (int)pack_bf16(x[4], x[5]),
+                                 (int)pack_bf16(x[6], x[7])};
+                bstore(ro, off, v);
+            } else {
+                bstore(ro, off, i32x4{__float_as_int(x[0]), __float_as_int(x[1]), __float_as_int(x[2]), __float_as_int(x[3])});
+                bstore(ro, col_ok ? off + 16u : kOOB, i32x4{__float_as_int(x[4]), __float_as_int(x[5]), __float_as_int(x[6]), __float_as_int(x[7])});
+            }
+        }
     }
 }
 
