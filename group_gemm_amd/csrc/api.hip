@@ -12,6 +12,7 @@ namespace {
 
 constexpr size_t kHeader = 256;   // workspace bytes before any padded buffer (status word first)
 constexpr int64_t kMaxCopies = int64_t(1) << 30;   // moe_permute: tokens * top_k
+constexpr size_t kQueueOffset = 64;                 // workspace header bytes before the 8 tile queues
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -65,9 +66,11 @@ struct EpiArgs {
     float alpha = 1.f, beta = 0.f;
 };
 
+// `status` may be NULL (the padded form's batched stage leaves the word to the scatter);
+// `ws` is the caller's workspace, whose header also holds the bf16 kernel's tile queues.
 gg_status run_m(const void* lhs, const void* rhs, const int32_t* gs, void* out, int64_t m, int64_t k, int64_t n,
                 int32_t g, gg_dtype in, gg_dtype outd, const uint8_t* ls, const uint8_t* rs, uint32_t* status,
-                int uniform_rows, hipStream_t s, bool rhs_nk = false, const EpiArgs& ep = EpiArgs()) {
+                void* ws, int uniform_rows, hipStream_t s, bool rhs_nk = false, const EpiArgs& ep = EpiArgs()) {
     int cus;
     if (device_cus(&cus) != 0) return GG_ERR_HIP;
     gg::MParams p{};
@@ -76,6 +79,7 @@ gg_status run_m(const void* lhs, const void* rhs, const int32_t* gs, void* out, 
     p.out_f32 = outd == GG_DT_F32;
     p.rhs_nk = rhs_nk ? 1 : 0;
     p.epi = ep.on ? 1 : 0; p.bias = ep.bias; p.bias_stride = ep.bias_stride; p.alpha = ep.alpha; p.beta = ep.beta;
+    p.tile_queue = (int*)((char*)ws + kQueueOffset);
     hipError_t e;
     if (rhs_nk) {   // [g,n,k] weights: the bf16 ring kernel only
         const bool vec = aligned(lhs, 16) && aligned(rhs, 16) && aligned(out, 16) && k % 8 == 0 && n % 8 == 0;
@@ -217,7 +221,7 @@ gg_status ragged_dot_m(const void* lhs, const void* rhs, const int32_t* group_si
         if ((m * k > 0 && !lhs_scale) || (k * n > 0 && !rhs_scale)) return GG_ERR_NULL_PTR;
         if (!aligned(lhs, 16) || !aligned(rhs, 16)) return GG_ERR_MISALIGNED;
     }
-    return run_m(lhs, rhs, group_sizes, out, m, k, n, g, in_dtype, out_dtype, lhs_scale, rhs_scale, (uint32_t*)workspace,
+    return run_m(lhs, rhs, group_sizes, out, m, k, n, g, in_dtype, out_dtype, lhs_scale, rhs_scale, (uint32_t*)workspace, workspace,
                  0, (hipStream_t)stream);
 }
 
@@ -231,7 +235,7 @@ gg_status ragged_dot_m_nk(const void* lhs, const void* rhs_nk, const int32_t* gr
     if ((m * k > 0 && !lhs) || (k * n > 0 && !rhs_nk) || (m * n > 0 && !out)) return GG_ERR_NULL_PTR;
     if (!aligned(lhs, 16) || !aligned(rhs_nk, 16) || !aligned(out, 16)) return GG_ERR_MISALIGNED;
     if (k % 8 != 0 || n % 8 != 0) return GG_ERR_UNSUPPORTED;
-    return run_m(lhs, rhs_nk, group_sizes, out, m, k, n, g, in_dtype, out_dtype, nullptr, nullptr, (uint32_t*)workspace,
+    return run_m(lhs, rhs_nk, group_sizes, out, m, k, n, g, in_dtype, out_dtype, nullptr, nullptr, (uint32_t*)workspace, workspace,
                  0, (hipStream_t)stream, true);
 }
 
@@ -254,7 +258,7 @@ gg_status ragged_dot_m_epilogue(const void* lhs, const void* rhs, const int32_t*
         if ((m * k > 0 && !lhs_scale) || (k * n > 0 && !rhs_scale)) return GG_ERR_NULL_PTR;
         if (!aligned(lhs, 16) || !aligned(rhs, 16)) return GG_ERR_MISALIGNED;
     }
-    return run_m(lhs, rhs, group_sizes, out, m, k, n, g, in_dtype, out_dtype, lhs_scale, rhs_scale, (uint32_t*)workspace,
+    return run_m(lhs, rhs, group_sizes, out, m, k, n, g, in_dtype, out_dtype, lhs_scale, rhs_scale, (uint32_t*)workspace, workspace,
                  0, (hipStream_t)stream, false, ep);
 }
 
@@ -352,7 +356,7 @@ gg_status padded_dot(gg_op mode, const void* a, const void* b, const int32_t* gr
             if (e != hipSuccess) return GG_ERR_HIP;
         }
         // 2. one uniform batched GEMM [g, C, k] x [g, k, n] -> [g, C, n]
-        st = run_m(pa, b, group_sizes, pb, rows, k, n, g, in_dtype, out_dtype, psc, b_scale, nullptr, (int)capacity, s);
+        st = run_m(pa, b, group_sizes, pb, rows, k, n, g, in_dtype, out_dtype, psc, b_scale, nullptr, workspace, (int)capacity, s);
         if (st != GG_OK) return st;
         // 3. compact: [g, C, n] -> [m, n]
         e = gg::launch_pad_gather(pb, out, group_sizes, (int)m, g, (int)capacity, (long long)n * (long long)os, s);

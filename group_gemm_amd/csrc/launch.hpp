@@ -26,6 +26,9 @@ struct MParams {
     const float* bias;          // [g, bias_stride] fp32 rows, or NULL
     int64_t bias_stride;
     float alpha, beta;
+    // 8 device ints the launcher zeroes: one tile queue per XCD (see the bf16 ring kernel),
+    // or NULL for the static walk
+    int* tile_queue;
 };
 
 // Contracting ragged dot: out[g,k,n] = per-group lhs[rows,k]^T . dout[rows,n].

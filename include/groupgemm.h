@@ -24,6 +24,9 @@
  *     size counts as 0 and the groups are cut off at row m (no access out of bounds); the
  *     device status word of the workspace records it (GG_DEV_*).
  *   - Host-detectable errors return a code and enqueue nothing.
+ *   - The workspace carries per-call state (the status word; the forward kernels' tile
+ *     queue counters, which each call resets on its stream): calls that share a workspace
+ *     must not run concurrently -- issue them on one stream or give each its own.
  *   - Accumulation is fp32.  bf16 outputs are rounded to nearest-even.
  *   - Tensors must be aligned to their element size (e4m3 operands: 16 bytes) and the
  *     workspace to 16 bytes.  16-byte aligned bf16 operands whose rows are whole multiples
