@@ -26,8 +26,8 @@ struct MParams {
     const float* bias;          // [g, bias_stride] fp32 rows, or NULL
     int64_t bias_stride;
     float alpha, beta;
-    // 8 device ints the launcher zeroes: one tile queue per XCD (see the bf16 ring kernel),
-    // or NULL for the static walk
+    // 8 device ints the launcher zeroes: one tile queue per XCD (the bf16 ring kernel's walk,
+    // ring.hpp), or NULL for the static walk; the other kernels walk statically
     int* tile_queue;
 };
 
@@ -63,6 +63,10 @@ struct GParams {
 };
 bool ragged_m_gated_ok(const GParams& p);
 hipError_t launch_ragged_m_gated(const GParams& p, int grid, hipStream_t s);
+
+// Zeroes the 8 tile-queue counters of a ring kernel (a one-block kernel, so the call can be
+// captured in a graph).
+hipError_t launch_clear_queues(int* queues, hipStream_t s);
 
 // Kernel families.  Each launcher returns the hipError_t of its launch.
 hipError_t launch_ragged_m_bf16(const MParams& p, int grid, bool vec, hipStream_t s);

@@ -37,7 +37,6 @@ namespace mb {
 using namespace ring;
 
 constexpr int BN = 256, BK = 32, NT = 256;
-constexpr int QCHUNK = 8;                 // consecutive tiles dealt to one XCD's queue
 constexpr int BSLICE = BK * BN;          // elements of one B slice: 16 KiB
 
 // B slice [32 k][256 n], 512-byte rows: 16-byte chunks XOR'ed in 64-byte units by a 3-bit
@@ -157,26 +156,10 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
         b_lane[u] = (uint32_t)(l >> 5) * n2 + (uint32_t)b_ch8[u] * 2u;
     }
 
-    // Tile walk.  With queues: the tiles are dealt to the 8 XCDs in chunks of QCHUNK
-    // consecutive tiles (chunk c to XCD c % 8; workgroup w runs on XCD w % 8), and every
-    // workgroup takes its XCD's next tile from an atomic counter.  A chunk's tiles share a
-    // row or weight panel and run side by side on one XCD, and workgroups that drew cheap
-    // tiles (a group's last, partly filled m-tile, or a short group) take more, where the
-    // static walk hands every workgroup the same number of tiles whatever they cost.
-    // Without queues (or with a grid that is not a multiple of 8): a static round-robin
-    // over virtual ids that keeps consecutive tiles on one XCD.
-    const bool queued = p.tile_queue != nullptr && (gridDim.x & 7) == 0;
-    const int xcd = blockIdx.x & 7;
-    for (int tile = queued ? 0 : xcd_virtual_id(blockIdx.x, gridDim.x);; tile += gridDim.x) {
-        if (queued) {
-            __syncthreads();   // every thread has read the previous index
-            if (t == 0) {
-                const int c = atomicAdd(p.tile_queue + xcd, 1);
-                sm.next_tile = ((c / QCHUNK) * 8 + xcd) * QCHUNK + c % QCHUNK;
-            }
-            __syncthreads();
-            tile = sm.next_tile;
-        }
+    // tile walk: per-XCD queues when the launcher provides them (see ring.hpp)
+    const bool queued = queued_walk(p.tile_queue);
+    for (int tile = first_tile(queued);; tile += gridDim.x) {
+        if (queued) tile = queue_next(p.tile_queue, &sm.next_tile);
         if (tile >= total) break;
         if (tile >= gemm_tiles) {   // rows past the covered ones: zeros
             const int z = tile - gemm_tiles;
@@ -342,9 +325,14 @@ __global__ void clear_queues(int* q) {
     if (threadIdx.x < 8) q[threadIdx.x] = 0;
 }
 
+hipError_t launch_clear_queues(int* q, hipStream_t s) {
+    hipLaunchKernelGGL(clear_queues, dim3(1), dim3(64), 0, s, q);
+    return hipGetLastError();
+}
+
 template <bool B_NK, bool EPI>
 static void launch_mb(const MParams& p, int grid, hipStream_t s) {
-    if (p.tile_queue) hipLaunchKernelGGL(clear_queues, dim3(1), dim3(64), 0, s, p.tile_queue);
+    if (p.tile_queue) launch_clear_queues(p.tile_queue, s);
     if (p.out_f32) hipLaunchKernelGGL((mb::kernel<GG_TILE, B_NK, EPI, float>), dim3(grid), dim3(mb::NT), 0, s, p);
     else hipLaunchKernelGGL((mb::kernel<GG_TILE, B_NK, EPI, uint16_t>), dim3(grid), dim3(mb::NT), 0, s, p);
 }

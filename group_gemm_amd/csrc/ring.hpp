@@ -89,6 +89,30 @@ __device__ inline void with_nb(int nb, F&& fn) {
     }
 }
 
+// Tile walk of the persistent ring kernels.  With queues (8 device ints, one per XCD,
+// zeroed by launch_clear_queues before the launch): the tiles are dealt to the 8 XCDs in
+// chunks of kQueueChunk consecutive tiles (chunk c to XCD c % 8; workgroup w runs on XCD
+// w % 8) and every workgroup takes its XCD's next tile from an atomic counter.  A chunk's
+// tiles share a row or weight panel and run side by side on one XCD, and workgroups that
+// drew cheap tiles (a short group, a group's partly filled last m-tile) take more, where
+// the static walk hands every workgroup the same number of tiles whatever they cost.
+// Without queues, or with a grid that is not a multiple of 8: a static round-robin over
+// virtual ids that keeps consecutive tiles on one XCD.  All threads call these together.
+constexpr int kQueueChunk = 8;
+__device__ inline bool queued_walk(const int* queues) { return queues != nullptr && (gridDim.x & 7) == 0; }
+__device__ inline int first_tile(bool queued) { return queued ? 0 : xcd_virtual_id(blockIdx.x, gridDim.x); }
+// the next tile of a queued walk; `slot` is an int in LDS
+__device__ inline int queue_next(int* queues, int* slot) {
+    __syncthreads();   // every thread has read the previous index
+    if (threadIdx.x == 0) {
+        const int xcd = blockIdx.x & 7;
+        const int c = atomicAdd(queues + xcd, 1);
+        *slot = ((c / kQueueChunk) * 8 + xcd) * kQueueChunk + c % kQueueChunk;
+    }
+    __syncthreads();
+    return *slot;
+}
+
 // Optional epilogue of the tile: out = alpha * acc + bias_row[col] + beta * out (in place).
 struct EpiTile {
     const float* bias_row;   // this group's bias row, or nullptr
