@@ -36,7 +36,7 @@ namespace gg {
 namespace mb {
 using namespace ring;
 
-constexpr int BN = 256, BK = 32, NT = 256;
+constexpr int BN = 256, BK = 32;
 constexpr int BSLICE = BK * BN;          // elements of one B slice: 16 KiB
 
 // B slice [32 k][256 n], 512-byte rows: 16-byte chunks XOR'ed in 64-byte units by a 3-bit
@@ -48,22 +48,25 @@ __device__ inline int b_off(int kr, int nn) { return kr * BN + (((nn >> 3) ^ b_s
 // swizzle runs ds_read_b128 at ~115 B/clk per CU against ~76 for an XOR by (row >> 2) & 3.
 __device__ inline int a_off(int r, int chunk) { return r * BK + ((chunk ^ ((r >> 1) & 3)) << 3); }
 
-template <int BM, int WAVES_M, int STAGES>
+template <int BM, int WAVES_M, int STAGES, int NW>
 struct Cfg {
     static constexpr int BM_ROWS = BM;
-    static constexpr int WAVES_N = 4 / WAVES_M;
+    static constexpr int NT = 64 * NW;                            // threads of a workgroup
+    static constexpr int WAVES_N = NW / WAVES_M;
     static constexpr int WROWS = BM / WAVES_M, WCOLS = BN / WAVES_N;
     static constexpr int MI = WROWS / 32, NJ = WCOLS / 32;       // MFMA blocks per wave
     static constexpr int ASLICE = BM * BK;
-    static constexpr int A_LOADS = BM / 64;                       // 1 KiB A blocks per wave
-    static constexpr int PER = A_LOADS + 4;                       // ring loads per thread per slice
+    static constexpr int A_LOADS = BM / 16 / NW;                  // 1 KiB A blocks (16 rows) per wave
+    static constexpr int B_LOADS = 16 / NW;                       // 1 KiB B blocks per wave
+    static constexpr int PER = A_LOADS + B_LOADS;                 // ring loads per thread per slice
+    static_assert(BM % (16 * NW) == 0 && 16 % NW == 0 && NW % WAVES_M == 0, "wave roles");
     static_assert(BM % 64 == 0 && WROWS % 32 == 0 && WCOLS % 32 == 0, "tile shape");
     static_assert(PER * (STAGES - 1) <= 63, "vmcnt range");
 };
 
-template <int BM, int WAVES_M, int STAGES>
+template <int BM, int WAVES_M, int STAGES, int NW>
 struct Smem {
-    typedef Cfg<BM, WAVES_M, STAGES> C;
+    typedef Cfg<BM, WAVES_M, STAGES, NW> C;
     struct {
         uint16_t a[STAGES][C::ASLICE];
         uint16_t b[STAGES][BSLICE];
@@ -111,11 +114,11 @@ __device__ inline void read_one(Frags<MI, NJ>& f, const uint16_t* a, const uint1
 }
 
 
-template <int BM, int WAVES_M, int STAGES, bool B_NK, bool EPI, typename OutT>
-__global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
-    typedef Cfg<BM, WAVES_M, STAGES> C;
-    constexpr int MI = C::MI, NJ = C::NJ;
-    __shared__ Smem<BM, WAVES_M, STAGES> sm;
+template <int BM, int WAVES_M, int STAGES, int NW, bool B_NK, bool EPI, typename OutT>
+__global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
+    typedef Cfg<BM, WAVES_M, STAGES, NW> C;
+    constexpr int MI = C::MI, NJ = C::NJ, NT = C::NT;
+    __shared__ Smem<BM, WAVES_M, STAGES, NW> sm;
     const int t = threadIdx.x, l = t & 63, wave = t >> 6, h = l >> 5;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int r0w = wm * C::WROWS, c0w = wn * C::WCOLS;   // this wave's sub-tile origin
@@ -137,21 +140,21 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
     // Ring-load roles (fixed per thread).  A slice: 1 KiB blocks of 16 rows, wave w fills
     // blocks A_LOADS*w + u; lane l writes physical chunk l % 4 of row 16 b + l / 4, which
     // holds logical chunk (l & 3) ^ ((row >> 1) & 3) = (l & 3) ^ ((l >> 3) & 3).
-    // B slice: 1 KiB blocks of 2 rows, wave w fills blocks 4w..4w+3; lane l writes
+    // B slice: 1 KiB blocks of 2 rows, wave w fills blocks B_LOADS w + u; lane l writes
     // physical chunk l % 32 of row 2b + l / 32, which holds logical chunk (l & 31) ^ b_swz.
     const int a_chunk = (l & 3) ^ ((l >> 3) & 3);
     // this wave's first 1 KiB block in A / B slot 0 (wave-uniform, scalar registers)
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t lds_a = lds_u32(&sm.ring.a[0][0]) + (uint32_t)(C::A_LOADS * wave_u) * 1024u;
-    const uint32_t lds_b = lds_u32(&sm.ring.b[0][0]) + (uint32_t)(4 * wave_u) * 1024u;
+    const uint32_t lds_b = lds_u32(&sm.ring.b[0][0]) + (uint32_t)(C::B_LOADS * wave_u) * 1024u;
     // per-lane parts of the ring-load offsets (the wave- and tile-uniform parts are added
     // at each load, in scalar registers)
     const uint32_t a_lane = (uint32_t)(l >> 2) * k2 + (uint32_t)a_chunk * 16u;
-    uint32_t b_lane[4];
-    int b_ch8[4];
+    uint32_t b_lane[C::B_LOADS];
+    int b_ch8[C::B_LOADS];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int b_row = 2 * (4 * wave + u) + (l >> 5);
+    for (int u = 0; u < C::B_LOADS; ++u) {
+        const int b_row = 2 * (C::B_LOADS * wave + u) + (l >> 5);
         b_ch8[u] = 8 * ((l & 31) ^ b_swz(b_row));
         b_lane[u] = (uint32_t)(l >> 5) * n2 + (uint32_t)b_ch8[u] * 2u;
     }
@@ -208,13 +211,13 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
                 // rows past n fall outside the descriptor
                 constexpr int u = d - C::A_LOADS;
                 const bool ok = live && kk + 8 * a_chunk < p.k;
-                const uint32_t wpart = (uint32_t)(col0 + 16 * (4 * wave_u + u)) * k2 + (uint32_t)kk * 2u;
+                const uint32_t wpart = (uint32_t)(col0 + 16 * (C::B_LOADS * wave_u + u)) * k2 + (uint32_t)kk * 2u;
                 load_lds16(rb, lds_b + (uint32_t)slot * (BSLICE * 2) + u * 1024u, ok ? a_lane + wpart : kOOB);
             } else {
                 // k row kk + 2 (4 wave + u) + l / 32, columns col0 + b_ch8 .. + 7
                 constexpr int u = d - C::A_LOADS;
                 const bool ok = live && b_ch8[u] < p.n - col0;
-                const uint32_t wpart = (uint32_t)(kk + 2 * (4 * wave_u + u)) * n2 + (uint32_t)col0 * 2u;
+                const uint32_t wpart = (uint32_t)(kk + 2 * (C::B_LOADS * wave_u + u)) * n2 + (uint32_t)col0 * 2u;
                 load_lds16(rb, lds_b + (uint32_t)slot * (BSLICE * 2) + u * 1024u, ok ? b_lane[u] + wpart : kOOB);
             }
         };
@@ -293,7 +296,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
         lds_barrier();
 
         const rsrc_t ro = make_rsrc((const char*)p.out + (size_t)row0 * p.n * osz, (uint32_t)(rows_valid * p.n * osz));
-        static_assert(4 * 32 * (C::WCOLS + 4) * 4 <= (int)sizeof(sm.ring), "epilogue strips fit the ring");
+        static_assert(NW * 32 * (C::WCOLS + 4) * 4 <= (int)sizeof(sm.ring), "epilogue strips fit the ring");
         const EpiTile ep{p.bias ? p.bias + (size_t)grp * p.bias_stride : nullptr, p.alpha, p.beta};
         store_acc<MI, NJ, C::WCOLS, OutT, EPI>(acc, reinterpret_cast<float*>(&sm.ring) + wave * 32 * (C::WCOLS + 4), ro, p.n,
                                                col0, r0w, c0w, ep);
@@ -302,12 +305,14 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
     wait_vm<0>();   // no ring load may still be writing LDS when the workgroup ends
 }
 
-// tile shape: (rows, waves along rows, ring slots).  256 x 256 with a 4-slot ring is the
-// fastest of the shapes the template allows (64 / 128 / 256 rows, 1 / 2 / 4 row waves, 3-7
-// slots) both on groups of ~1000 rows, where the MFMA bounds it, and on Zipf-skewed groups
-// of ~128 rows, where the weight stream does: blocks past a group's last row are skipped,
-// so tall tiles cost short groups little, while they halve the B fragment reads per flop.
-#define GG_TILE 256, 2, 4
+// tile shape: (rows, waves along rows, ring slots, waves).  256 x 256 with a 4-slot ring and
+// four waves is the fastest of the shapes the template allows (64 / 128 / 256 rows, 1 / 2 / 4
+// row waves, 3-7 slots, 4 or 8 waves) both on groups of ~1000 rows, where the MFMA bounds
+// it, and on Zipf-skewed groups of ~128 rows, where the weight stream does: blocks past a
+// group's last row are skipped, so tall tiles cost short groups little, while they halve
+// the B fragment reads per flop.  (Eight waves, two per SIMD with the accumulators in
+// VGPRs, ran 5 % slower on the first and 25 % on the second.)
+#define GG_TILE 256, 2, 4, 4
 
 }  // namespace mb
 
@@ -333,8 +338,9 @@ hipError_t launch_clear_queues(int* q, hipStream_t s) {
 template <bool B_NK, bool EPI>
 static void launch_mb(const MParams& p, int grid, hipStream_t s) {
     if (p.tile_queue) launch_clear_queues(p.tile_queue, s);
-    if (p.out_f32) hipLaunchKernelGGL((mb::kernel<GG_TILE, B_NK, EPI, float>), dim3(grid), dim3(mb::NT), 0, s, p);
-    else hipLaunchKernelGGL((mb::kernel<GG_TILE, B_NK, EPI, uint16_t>), dim3(grid), dim3(mb::NT), 0, s, p);
+    constexpr int nt = mb::Cfg<GG_TILE>::NT;
+    if (p.out_f32) hipLaunchKernelGGL((mb::kernel<GG_TILE, B_NK, EPI, float>), dim3(grid), dim3(nt), 0, s, p);
+    else hipLaunchKernelGGL((mb::kernel<GG_TILE, B_NK, EPI, uint16_t>), dim3(grid), dim3(nt), 0, s, p);
 }
 
 hipError_t launch_ragged_m_bf16_fast(const MParams& p, int grid, hipStream_t s) {
