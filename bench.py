@@ -168,27 +168,28 @@ def cpu_baseline_routing(w, d, target_s, raw, oracle):
 
 
 def kernels_digest():
-    """sha256 over the kernel sources; a traffic record taken from other sources is stale."""
+    """sha256 of the built library, whose gfx950 code objects hold the kernels; a traffic
+    record taken with another build is stale.  (Builds are deterministic, so edits that
+    leave the code unchanged, such as comments, keep the record valid.)"""
     import hashlib
-    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "group_gemm_amd", "csrc")
-    h = hashlib.sha256()
-    for fn in sorted(os.listdir(d)):
-        if fn.endswith((".hip", ".hpp", ".h")):
-            h.update(fn.encode())
-            with open(os.path.join(d, fn), "rb") as f:
-                h.update(f.read())
-    return h.hexdigest()
+    lib = os.path.join(os.path.dirname(os.path.abspath(__file__)), "group_gemm_amd", "libgroupgemm.so")
+    try:
+        with open(lib, "rb") as f:
+            return hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
 
 
 def traffic_for(name):
     """HBM bytes per launch of the workload's dominant kernel, measured with rocprofv3
-    counters on the current kernel sources; None when there is no such measurement."""
+    counters on the current build; None when there is no such measurement."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             rec = json.load(f).get(name)
     except (OSError, ValueError):
         return None
-    if rec is None or rec.get("kernels_sha256") != kernels_digest():
+    digest = kernels_digest()
+    if rec is None or digest is None or rec.get("kernels_sha256") != digest:
         return None
     return rec.get("bytes_per_launch")
 

@@ -33,13 +33,12 @@ namespace gg {
 namespace perm {
 
 constexpr int NT = 1024;    // threads of the histogram and rank workgroups
-// Cache policy of the row copies' whole-line stores: each sorted row is written once and not
-// read again here, so the stores carry gfx950's nontemporal (`nt`) hint, which lets them
-// stream past the caches (measured +13 % on the permute, +12 % on the un-permute).  The
-// GEMM kernels do not use it: their fp32 tile stores are partial lines per instruction and
-// ran at half speed with it.
-constexpr int kNontemporal = 2;
 constexpr int NW = NT / 64;
+// Cache policy of the row copies: each sorted row is written once and each expert-output row
+// read once, so these accesses carry gfx950's nontemporal (`nt`) hint, which streams them
+// past the caches (measured +13 % on the permute, +12 % on the un-permute).  The GEMM
+// kernels' output stores do not use it: there it measured neutral to twice as slow.
+constexpr int kNontemporal = 2;
 // row kernels (scatter, combine): 256-thread workgroups, WPR waves share one token's row
 constexpr int WPR = 2;
 constexpr int TPB = 4 / WPR;   // tokens per workgroup
