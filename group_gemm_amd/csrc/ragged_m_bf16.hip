@@ -12,9 +12,11 @@
 // consumed in 32-wide slices.  The kernel is a template over tile rows, wave layout and
 // ring depth so other shapes can be timed; one shape is instantiated (see GG_TILE).
 //  * Operands stream through an LDS ring filled by buffer loads that write LDS directly
-//    (no staging registers), STAGES - 1 slices ahead of the MFMAs.  The buffer
-//    descriptors bound the group's rows and the weight matrix, so rows past the group and
-//    the k / n tails arrive as zeros without branches.
+//    (no staging registers): B (weights) one k slice per slot, three slices ahead of the
+//    MFMAs; A (rows) two k slices per slot, so that every load moves 128 contiguous bytes
+//    of a row, landing two iterations before use.  The buffer descriptors bound the
+//    group's rows and the weight matrix, so rows past the group and the k / n tails
+//    arrive as zeros without branches.
 //  * A rows (k-contiguous) feed the MFMA through ds_read_b128; B rows are n-contiguous
 //    (rhs as given, no per-call relayout) and ds_read_b64_tr_b16 turns them into
 //    k-consecutive fragments.
@@ -43,10 +45,17 @@ constexpr int BSLICE = BK * BN;          // elements of one B slice: 16 KiB
 // function of the row, so the rows one transpose read touches land in distinct bank groups.
 __device__ inline int b_swz(int kr) { return ((kr & 3) | (((kr >> 3) & 1) << 2)) << 2; }
 __device__ inline int b_off(int kr, int nn) { return kr * BN + (((nn >> 3) ^ b_swz(kr)) << 3) + (nn & 7); }
-// A slice [BM rows][32 k], 64-byte rows: 16-byte chunk XOR (row >> 1) & 3.  Measured on
-// gfx950 with the fragment reads below (32 consecutive rows, one chunk per lane half), this
-// swizzle runs ds_read_b128 at ~115 B/clk per CU against ~76 for an XOR by (row >> 2) & 3.
+// [rows][32 k] slice, 64-byte rows (the [n][k] weights of the data-gradient form): 16-byte
+// chunk XOR (row >> 1) & 3.  Measured on gfx950 with the fragment reads below (32
+// consecutive rows, one chunk per lane half), this swizzle runs ds_read_b128 at ~115 B/clk
+// per CU against ~76 for an XOR by (row >> 2) & 3.
 __device__ inline int a_off(int r, int chunk) { return r * BK + ((chunk ^ ((r >> 1) & 3)) << 3); }
+// A pair [BM rows][64 k] (two k slices), 128-byte rows: 16-byte chunk XOR (row >> 1) & 7, so
+// the 16 rows a quarter of a fragment read touches fill the 64 banks once.  The A ring holds
+// pairs because a load of 128 contiguous bytes per row moves twice the data per row as one of
+// 64: measured on gfx950 with loads straight into LDS from L2-resident data, 16 rows x 64 B
+// per instruction stream at ~30 B/clk per CU, 8 rows x 128 B at ~60.
+__device__ inline int ap_off(int r, int chunk) { return r * (2 * BK) + ((chunk ^ ((r >> 1) & 7)) << 3); }
 
 template <int BM, int WAVES_M, int STAGES, int NW>
 struct Cfg {
@@ -55,21 +64,23 @@ struct Cfg {
     static constexpr int WAVES_N = NW / WAVES_M;
     static constexpr int WROWS = BM / WAVES_M, WCOLS = BN / WAVES_N;
     static constexpr int MI = WROWS / 32, NJ = WCOLS / 32;       // MFMA blocks per wave
-    static constexpr int ASLICE = BM * BK;
-    static constexpr int A_LOADS = BM / 16 / NW;                  // 1 KiB A blocks (16 rows) per wave
-    static constexpr int B_LOADS = 16 / NW;                       // 1 KiB B blocks per wave
-    static constexpr int PER = A_LOADS + B_LOADS;                 // ring loads per thread per slice
-    static_assert(BM % (16 * NW) == 0 && 16 % NW == 0 && NW % WAVES_M == 0, "wave roles");
+    static constexpr int APAIR = BM * 2 * BK;                     // elements of one A pair (two k slices)
+    static constexpr int A_LOADS = BM / 8 / NW;                   // 1 KiB A blocks (8 rows x 128 B) per wave and pair
+    static constexpr int A_HALF = A_LOADS / 2;                    // A loads per iteration
+    static constexpr int B_LOADS = 16 / NW;                       // 1 KiB B blocks per wave and slice
+    static constexpr int BNK_LOADS = BN / 16 / NW;                // [n][k] weights: 1 KiB blocks of 16 rows
+    static_assert(STAGES == 3 && NW == 4 && BM == 256, "the ring schedule assumes 3 slots, 4 waves, 256 rows");
+    static_assert(BM % (8 * NW) == 0 && A_LOADS % 2 == 0 && 16 % NW == 0 && NW % WAVES_M == 0, "wave roles");
+    static_assert(A_HALF == B_LOADS && BNK_LOADS == B_LOADS, "as many A as B loads per iteration");
     static_assert(BM % 64 == 0 && WROWS % 32 == 0 && WCOLS % 32 == 0, "tile shape");
-    static_assert(PER * (STAGES - 1) <= 63, "vmcnt range");
 };
 
 template <int BM, int WAVES_M, int STAGES, int NW>
 struct Smem {
     typedef Cfg<BM, WAVES_M, STAGES, NW> C;
     struct {
-        uint16_t a[STAGES][C::ASLICE];
-        uint16_t b[STAGES][BSLICE];
+        uint16_t a[STAGES][C::APAIR];   // A pairs of k slices
+        uint16_t b[STAGES][BSLICE];     // B slices
     } ring;
     Tables tab;
     int next_tile;
@@ -89,13 +100,14 @@ __device__ inline void mma(const Frags<MI, NJ>& f, f32x16 (&acc)[MI][NJ]) {
 }
 
 
-// fragment read number R of k step s, in the order the MFMAs (column block major) first
-// need them: B block 0, A blocks 0 .. NB - 1, then B blocks 1 .. NJ - 1
+// fragment read number R of k step s of a slice, in the order the MFMAs (column block
+// major) first need them: B block 0, A blocks 0 .. NB - 1, then B blocks 1 .. NJ - 1.  `a` is
+// the slice's A pair and ac = 4 (slice parity) + 2 s its first 16-byte chunk of the step.
 template <int MI, int NJ, int NB, int R, bool B_NK>
-__device__ inline void read_one(Frags<MI, NJ>& f, const uint16_t* a, const uint16_t* b, int s, int r0, int c0) {
+__device__ inline void read_one(Frags<MI, NJ>& f, const uint16_t* a, const uint16_t* b, int ac, int s, int r0, int c0) {
     const int l = threadIdx.x & 63, h = l >> 5;
     if constexpr (R >= 1 && R <= NB) {
-        f.a[R - 1] = *(const bf16x8*)(a + a_off(r0 + 32 * (R - 1) + (l & 31), 2 * s + h));
+        f.a[R - 1] = *(const bf16x8*)(a + ap_off(r0 + 32 * (R - 1) + (l & 31), ac + h));
     } else if constexpr (B_NK) {
         // k-contiguous weights: the slice is [256 n][32 k] in the A layout
         constexpr int j = R == 0 ? 0 : R - NB;
@@ -137,19 +149,29 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
     const uint32_t k2 = (uint32_t)p.k * 2u, n2 = (uint32_t)p.n * 2u;
     constexpr int osz = sizeof(OutT);
 
-    // Ring-load roles (fixed per thread).  A slice: 1 KiB blocks of 16 rows, wave w fills
-    // blocks A_LOADS*w + u; lane l writes physical chunk l % 4 of row 16 b + l / 4, which
-    // holds logical chunk (l & 3) ^ ((row >> 1) & 3) = (l & 3) ^ ((l >> 3) & 3).
-    // B slice: 1 KiB blocks of 2 rows, wave w fills blocks B_LOADS w + u; lane l writes
-    // physical chunk l % 32 of row 2b + l / 32, which holds logical chunk (l & 31) ^ b_swz.
-    const int a_chunk = (l & 3) ^ ((l >> 3) & 3);
+    // Ring-load roles (fixed per thread).
+    // A pair [256 rows][64 k]: 1 KiB blocks of 8 rows x 128 B, wave w fills blocks
+    // A_LOADS w + e; lane l writes physical chunk l % 8 of row 8 b + l / 8, which holds
+    // logical chunk (l & 7) ^ ((row >> 1) & 7) = (l & 7) ^ ((4 (e & 1) + l / 16) & 7).
+    // B slice [32 k][256 n]: 1 KiB blocks of 2 rows, wave w fills blocks B_LOADS w + u; lane
+    // l writes physical chunk l % 32 of row 2 b + l / 32, which holds logical chunk
+    // (l & 31) ^ b_swz.  [n][k] weights (B_NK): 1 KiB blocks of 16 rows x 64 B; lane l writes
+    // physical chunk l % 4 of row 16 b + l / 4, logical chunk (l & 3) ^ ((row >> 1) & 3).
+    int ap_ch[2];
+    uint32_t ap_lane[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        ap_ch[e] = (l & 7) ^ ((4 * e + (l >> 4)) & 7);
+        ap_lane[e] = (uint32_t)(l >> 3) * k2 + (uint32_t)ap_ch[e] * 16u;
+    }
+    const int nk_chunk = (l & 3) ^ ((l >> 3) & 3);
+    const uint32_t nk_lane = (uint32_t)(l >> 2) * k2 + (uint32_t)nk_chunk * 16u;
     // this wave's first 1 KiB block in A / B slot 0 (wave-uniform, scalar registers)
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t lds_a = lds_u32(&sm.ring.a[0][0]) + (uint32_t)(C::A_LOADS * wave_u) * 1024u;
     const uint32_t lds_b = lds_u32(&sm.ring.b[0][0]) + (uint32_t)(C::B_LOADS * wave_u) * 1024u;
-    // per-lane parts of the ring-load offsets (the wave- and tile-uniform parts are added
+    // per-lane parts of the B ring-load offsets (the wave- and tile-uniform parts are added
     // at each load, in scalar registers)
-    const uint32_t a_lane = (uint32_t)(l >> 2) * k2 + (uint32_t)a_chunk * 16u;
     uint32_t b_lane[C::B_LOADS];
     int b_ch8[C::B_LOADS];
 #pragma unroll
@@ -194,31 +216,33 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
 
         const i32x4 ra = make_rsrc_v((const uint16_t*)p.lhs + (size_t)row0 * p.k, (uint32_t)rows_valid * k2);
         const i32x4 rb = make_rsrc_v((const uint16_t*)p.rhs + (size_t)grp * p.k * p.n, (uint32_t)p.k * n2);
-        // ring load number d (A blocks first, then B) of k slice `stage` into its slot;
-        // slices past k are zero-filled into the slot no one reads, which keeps the number
-        // of loads per iteration, and so every wait count, constant
-        auto dma_one = [&](auto d_c, int stage) {
-            constexpr int d = decltype(d_c)::value;
-            const int kk = stage * BK, slot = stage % STAGES;
-            const bool live = stage < nk;
-            if constexpr (d < C::A_LOADS) {
-                // row 16 (A_LOADS wave + d) + l / 4 of the tile, chunk a_chunk
-                const bool ok = live && kk + 8 * a_chunk < p.k;
-                const uint32_t wpart = (uint32_t)(16 * (C::A_LOADS * wave_u + d)) * k2 + (uint32_t)kk * 2u;
-                load_lds16(ra, lds_a + (uint32_t)slot * (C::ASLICE * 2) + d * 1024u, ok ? a_lane + wpart : kOOB);
-            } else if constexpr (B_NK) {
-                // [n][k] weights: row col0 + 16 (4 wave + u) + l / 4, chunk a_chunk (the A roles);
-                // rows past n fall outside the descriptor
-                constexpr int u = d - C::A_LOADS;
-                const bool ok = live && kk + 8 * a_chunk < p.k;
+        // Ring loads.  Every iteration issues the same number, and loads past the end of k
+        // read zeros into a slot no one reads, so every wait count is a compile-time constant.
+        // A block e of pair `pr` (k slices 2 pr, 2 pr + 1): rows 8 (A_LOADS wave + e) + l / 8
+        // of the tile, logical chunk ap_ch[e & 1]
+        auto dma_a = [&](auto e_c, int pr) {
+            constexpr int e = decltype(e_c)::value;
+            const int kk = pr * 2 * BK;
+            const bool ok = kk + 8 * ap_ch[e & 1] < p.k;
+            const uint32_t wpart = (uint32_t)(8 * (C::A_LOADS * wave_u + e)) * k2 + (uint32_t)kk * 2u;
+            load_lds16(ra, lds_a + (uint32_t)(pr % STAGES) * (C::APAIR * 2) + e * 1024u, ok ? ap_lane[e & 1] + wpart : kOOB);
+        };
+        // B block u of k slice st
+        auto dma_b = [&](auto u_c, int st) {
+            constexpr int u = decltype(u_c)::value;
+            const int kk = st * BK;
+            const uint32_t dst = lds_b + (uint32_t)(st % STAGES) * (BSLICE * 2) + u * 1024u;
+            if constexpr (B_NK) {
+                // [n][k] weights: row col0 + 16 (4 wave + u) + l / 4, chunk nk_chunk; rows past n
+                // fall outside the descriptor
+                const bool ok = kk + 8 * nk_chunk < p.k;
                 const uint32_t wpart = (uint32_t)(col0 + 16 * (C::B_LOADS * wave_u + u)) * k2 + (uint32_t)kk * 2u;
-                load_lds16(rb, lds_b + (uint32_t)slot * (BSLICE * 2) + u * 1024u, ok ? a_lane + wpart : kOOB);
+                load_lds16(rb, dst, ok ? nk_lane + wpart : kOOB);
             } else {
                 // k row kk + 2 (4 wave + u) + l / 32, columns col0 + b_ch8 .. + 7
-                constexpr int u = d - C::A_LOADS;
-                const bool ok = live && b_ch8[u] < p.n - col0;
+                const bool ok = kk < p.k && b_ch8[u] < p.n - col0;
                 const uint32_t wpart = (uint32_t)(kk + 2 * (C::B_LOADS * wave_u + u)) * n2 + (uint32_t)col0 * 2u;
-                load_lds16(rb, lds_b + (uint32_t)slot * (BSLICE * 2) + u * 1024u, ok ? b_lane[u] + wpart : kOOB);
+                load_lds16(rb, dst, ok ? b_lane[u] + wpart : kOOB);
             }
         };
 
@@ -230,17 +254,16 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-        // One half slice: the MFMAs on `cur` with, after some, one ring load of slice `stage`
-        // and, after each, at most one fragment read of `nxt` (k step s of slot a / b).  HALF
-        // selects the ring loads: 0 none, 1 the first PER / 2 (the A blocks), 2 the rest; they
-        // are spread evenly over the MFMAs, so the four waves' loads reach the memory pipeline
-        // one at a time rather than in a burst.  The order is pinned so the loads and reads
-        // issue while the MFMAs run.
-        auto phase = [&](auto nb_c, auto half_c, Frags<MI, NJ>& cur, Frags<MI, NJ>& nxt, const uint16_t* a,
-                         const uint16_t* b, int s, int stage) {
+        // One half slice: the MFMAs on `cur` with, after each, at most one fragment read of
+        // `nxt` (k step s: chunk ac of A pair a, step s of B slot b) and, spread evenly over
+        // the MFMAs, ND ring loads mem(d) for d = 0 .. ND - 1, so the four waves' loads reach
+        // the memory pipeline one at a time rather than in a burst.  The order is pinned so
+        // the loads and reads issue while the MFMAs run.
+        auto phase = [&](auto nb_c, auto nd_c, auto&& mem, Frags<MI, NJ>& cur, Frags<MI, NJ>& nxt, const uint16_t* a,
+                         int ac, const uint16_t* b, int s) {
             constexpr int NB = decltype(nb_c)::value;
-            constexpr int HALF = decltype(half_c)::value;
-            constexpr int NM = NB * NJ, NR = NB > 0 ? NB + NJ : 0, ND = HALF ? C::PER / 2 : 0;
+            constexpr int ND = decltype(nd_c)::value;
+            constexpr int NM = NB * NJ, NR = NB > 0 ? NB + NJ : 0;
             constexpr int SP = ND > 0 && NM >= ND ? NM / ND : 1;   // MFMAs between two ring loads
             constexpr int LD = ND > 0 ? (ND - 1) * SP + 1 : 0;
             constexpr int NOPS = NM > NR ? (NM > LD ? NM : LD) : (NR > LD ? NR : LD);
@@ -250,42 +273,67 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
                     constexpr int i = o % (NB > 0 ? NB : 1), j = o / (NB > 0 ? NB : 1);
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
                 }
-                if constexpr (ND > 0 && o % SP == 0 && o / SP < ND)
-                    dma_one(std::integral_constant<int, (HALF - 1) * (C::PER / 2) + o / SP>{}, stage);
-                if constexpr (o < NR) read_one<MI, NJ, NB, o, B_NK>(nxt, a, b, s, r0w, c0w);
+                if constexpr (ND > 0 && o % SP == 0 && o / SP < ND) mem(std::integral_constant<int, o / SP>{});
+                if constexpr (o < NR) read_one<MI, NJ, NB, o, B_NK>(nxt, a, b, ac, s, r0w, c0w);
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
 
-        // Slice s is loaded in two halves: the first in the second half slice of iteration
-        // s - 4 (its slot, read last in the first half slice of that iteration, is free once
-        // the iteration's barrier has passed), the second in the first half slice of
-        // iteration s - 3.  Either way PER * (STAGES - 2) loads are issued after slice kt + 1's
-        // last one by the time iteration kt waits for it.
-        static_assert(STAGES == 4 && C::PER % 2 == 0, "the split ring loads assume a 4-slot ring");
+        // Iteration kt runs k step 0 of slice kt, waits for slice kt + 1, then runs step 1
+        // while reading step 0 of slice kt + 1.  Ring loads, four per half slice:
+        //  * B slice kt + 3 in the second half slice of iteration kt.  Its slot held slice
+        //    kt, whose last reads came before this iteration's barrier.
+        //  * A pair j (slices 2 j, 2 j + 1) in the first half slices of iterations 2 j - 4
+        //    (blocks 0-3) and 2 j - 3 (blocks 4-7).  Its slot held pair j - 3, read last before
+        //    the barrier of iteration 2 j - 5.
+        // At the barrier of iteration kt slice kt + 1's B blocks, issued in iteration kt - 2,
+        // are followed by 12 loads (its A pair by at least 16), so a wait for 12 outstanding
+        // loads covers both; loads complete in issue order among themselves, and output
+        // stores of the previous tile still in flight only raise the count.
+        constexpr int AH = C::A_HALF, BL = C::B_LOADS;
+        constexpr int W_STEADY = 2 * AH + BL;   // B of slice kt + 1 is followed by A, B, A
         auto run = [&](auto nb_c) {
             constexpr int NB = decltype(nb_c)::value;
-            constexpr std::integral_constant<int, 0> none{};
-            constexpr std::integral_constant<int, 1> first{};
-            constexpr std::integral_constant<int, 2> second{};
+            constexpr std::integral_constant<int, 0> zero{};
+            constexpr std::integral_constant<int, AH> nd_a{};
+            constexpr std::integral_constant<int, BL> nd_b{};
             Frags<MI, NJ> f0, f1;
-            static_for<0, STAGES - 1>([&](auto st_c) { static_for<0, C::PER>([&](auto d_c) { dma_one(d_c, decltype(st_c)::value); }); });
-            static_for<0, C::PER / 2>([&](auto d_c) { dma_one(d_c, STAGES - 1); });
-            // slice 0 in LDS.  Loads complete in issue order among themselves; output stores of
-            // the previous tile still in flight only raise the count, so this can only wait longer.
-            wait_vm<C::PER * (STAGES - 2) + C::PER / 2>();
+            // what iterations before the first would have issued, in an order that leaves at
+            // least W_STEADY loads behind slice 1's B blocks before the first barrier
+            static_for<0, BL>([&](auto u_c) { dma_b(u_c, 0); });
+            static_for<0, 2 * AH>([&](auto e_c) { dma_a(e_c, 0); });
+            static_for<0, BL>([&](auto u_c) { dma_b(u_c, 1); });
+            static_for<0, 2 * AH>([&](auto e_c) { dma_a(e_c, 1); });
+            static_for<0, BL>([&](auto u_c) { dma_b(u_c, 2); });
+            wait_vm<2 * BL + 2 * AH>();   // slice 0's B blocks and pair 0 in LDS
             lds_barrier();
             if constexpr (NB > 0)
-                static_for<0, NB + NJ>([&](auto r_c) { read_one<MI, NJ, NB, decltype(r_c)::value, B_NK>(f0, sm.ring.a[0], sm.ring.b[0], 0, r0w, c0w); });
-            for (int kt = 0; kt + 1 < nk; ++kt) {
+                static_for<0, NB + NJ>([&](auto r_c) { read_one<MI, NJ, NB, decltype(r_c)::value, B_NK>(f0, sm.ring.a[0], sm.ring.b[0], 0, 0, r0w, c0w); });
+            // iteration kt with P = kt % 2 fixed at compile time (A chunk offsets and A block
+            // numbers depend on it)
+            auto iter = [&](auto par_c, int kt) {
+                constexpr int P = decltype(par_c)::value;
+                const int pa = (kt >> 1) % STAGES, pn = ((kt + 1) >> 1) % STAGES;
                 const int slot = kt % STAGES, ns = (kt + 1) % STAGES;
-                phase(nb_c, second, f0, f1, sm.ring.a[slot], sm.ring.b[slot], 1, kt + STAGES - 1);
-                wait_vm<C::PER * (STAGES - 2)>();   // slice kt + 1 in LDS
+                const int pr = (kt + 4) >> 1;   // A pair kt / 2 + 2, blocks 4 P .. 4 P + 3
+                phase(nb_c, nd_a, [&](auto d_c) { dma_a(std::integral_constant<int, P * AH + decltype(d_c)::value>{}, pr); },
+                      f0, f1, sm.ring.a[pa], 4 * P + 2, sm.ring.b[slot], 1);
+                wait_vm<W_STEADY>();   // slice kt + 1 in LDS
                 lds_barrier();
-                phase(nb_c, first, f1, f0, sm.ring.a[ns], sm.ring.b[ns], 0, kt + STAGES);
+                phase(nb_c, nd_b, [&](auto d_c) { dma_b(d_c, kt + 3); }, f1, f0, sm.ring.a[pn], 4 * (1 - P), sm.ring.b[ns], 0);
+            };
+            constexpr std::integral_constant<int, 0> even{};
+            constexpr std::integral_constant<int, 1> odd{};
+            int kt = 0;
+            for (; kt + 2 < nk; kt += 2) {
+                iter(even, kt);
+                iter(odd, kt + 1);
             }
-            const int last = (nk - 1) % STAGES;
-            phase(nb_c, none, f0, f1, sm.ring.a[last], sm.ring.b[last], 1, 0);
+            if (kt + 1 < nk) iter(even, kt);
+            const int last = nk - 1;
+            const uint16_t* al = sm.ring.a[(last >> 1) % STAGES];
+            const uint16_t* bl = sm.ring.b[last % STAGES];
+            phase(nb_c, zero, [&](auto) {}, f0, f1, al, 4 * (last & 1) + 2, bl, 1);
             mma<MI, NJ, NB>(f1, acc);
         };
         if (nk > 0) with_nb<MI>(nb, run);
@@ -305,14 +353,15 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
     wait_vm<0>();   // no ring load may still be writing LDS when the workgroup ends
 }
 
-// tile shape: (rows, waves along rows, ring slots, waves).  256 x 256 with a 4-slot ring and
-// four waves is the fastest of the shapes the template allows (64 / 128 / 256 rows, 1 / 2 / 4
-// row waves, 3-7 slots, 4 or 8 waves) both on groups of ~1000 rows, where the MFMA bounds
-// it, and on Zipf-skewed groups of ~128 rows, where the weight stream does: blocks past a
-// group's last row are skipped, so tall tiles cost short groups little, while they halve
-// the B fragment reads per flop.  (Eight waves, two per SIMD with the accumulators in
-// VGPRs, ran 5 % slower on the first and 25 % on the second.)
-#define GG_TILE 256, 2, 4, 4
+// tile shape: (rows, waves along rows, ring slots, waves).  256 x 256 with four waves was the
+// fastest shape (64 / 128 / 256 rows, 1 / 2 / 4 row waves, 3-7 single-slice slots, 4 or 8
+// waves, timed with an earlier ring of one k slice per slot) both on groups of ~1000 rows,
+// where the MFMA bounds it, and on Zipf-skewed groups of ~128 rows, where the weight stream
+// does: blocks past a group's last row are skipped, so tall tiles cost short groups
+// little, while they halve the B fragment reads per flop.  (Eight waves, two per SIMD with
+// the accumulators in VGPRs, ran 5 % slower on the first and 25 % on the second.)  The
+// three A-pair and three B slots take 144 KiB of the 160 KiB of LDS.
+#define GG_TILE 256, 2, 3, 4
 
 }  // namespace mb
 
