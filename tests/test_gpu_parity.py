@@ -117,6 +117,10 @@ M_CASES = [
     (90, 50, 24, [45, 45]),                      # k % 8 != 0 -> element-wise path
     (2048, 64, 64, [2] * 1024),                  # g = 1024
     (700, 128, 256, [1, 255, 256, 257, 0, 1]),   # sizes around the 256-row tile
+    # the A operand is staged in pairs of 32-wide k slices: a pair whose second slice is an
+    # 8-wide tail, and an odd slice count (the last pair half filled)
+    (260, 40, 256, [130, 0, 130]),
+    (300, 160, 264, [44, 256]),
     # a full persistent grid (tiles taken from the per-XCD queues), short and tall groups,
     # empty groups, and 1000 rows past the groups' total (zero tiles in the same walk)
     (4000, 128, 2304, [0, 17, 300, 1, 256, 129, 700, 5, 0, 64, 128, 127, 257, 33, 90, 200, 11, 0, 40, 60,
