@@ -44,8 +44,19 @@ struct Slot {
     uint8_t as[AS_BYTES];
     uint8_t bs[BS_BYTES];
 };
+// Row scales in blocks of 8 k slices (AS8, when k % 512 == 0 and the scales are 16-byte
+// aligned): the 16 bytes of a row's 16 k blocks come in one 16-byte load per row, issued
+// with the block's first slice into one of two buffers, instead of 4 bytes per row with
+// every slice.  A load straight into LDS costs about the same per cache line touched
+// whatever it moves of the line (measured on gfx950: ~0.5 lines per clock per CU), and the
+// per-slice form touches one line per row for 4 bytes, as many lines as the A data itself.
+// The other slices issue an out-of-range load into a dummy area, so every slice still
+// issues the same number of loads and every wait count stays constant.
+constexpr int AS8_BYTES = BM * 16;      // one block: 16 bytes per row
 struct Smem {
     Slot ring[STAGES];
+    uint8_t asb[2][AS8_BYTES];           // AS8: row scales of blocks j (buffer j % 2)
+    uint8_t asdummy[AS8_BYTES];          // AS8: target of the placeholder loads
     Tables tab;
 };
 
@@ -65,13 +76,16 @@ struct Frags {
 
 // A block i of a slot: lane l holds row r0w + 32 i + (l & 31), k bytes 16 h .. 16 h + 15 and
 // 32 + 16 h .. + 15 (h = l / 32), as the 32x32x64 f8f6f4 operand layout wants
-__device__ inline void read_a(Frags& f, int i, const Slot& s, int r0w, int ks) {
+template <bool AS8>
+__device__ inline void read_a(Frags& f, int i, const Slot& s, const Smem& sm, int r0w, int ks) {
     const int l = threadIdx.x & 63, h = l >> 5;
     const int r = r0w + 32 * i + (l & 31);
     const i32x4 lo = *(const i32x4*)(s.a + a_off(r, h));
     const i32x4 hi = *(const i32x4*)(s.a + a_off(r, 2 + h));
     f.a[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    f.sa[i] = s.as[4 * r + 2 * (ks & 1) + h];   // E8M0 of (row, k block 2 ks + h)
+    // E8M0 of (row, k block 2 ks + h)
+    if constexpr (AS8) f.sa[i] = sm.asb[(ks >> 3) & 1][16 * r + 2 * (ks & 7) + h];
+    else f.sa[i] = s.as[4 * r + 2 * (ks & 1) + h];
 }
 // B block j: lane l holds column c0w + 32 j + (l & 31) for the same k bytes, gathered by
 // four 8-byte transpose reads (lane j of a 16-lane group takes byte j % 8 of rows 2r + j / 8)
@@ -87,7 +101,7 @@ __device__ inline void read_b(Frags& f, int j, const Slot& s, int c0w, int cp) {
     f.sb[j] = s.bs[cp * 2 * BN + h * BN + c0w + 32 * j + (l & 31)];   // E8M0 of (column, k block 2 ks + h)
 }
 
-template <bool EPI, typename OutT>
+template <bool AS8, bool EPI, typename OutT>
 __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
     __shared__ Smem sm;
     const int t = threadIdx.x, l = t & 63, wave = t >> 6;
@@ -122,6 +136,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
         b_lane[u] = (uint32_t)(l >> 4) * (uint32_t)p.n + (uint32_t)b_col[u];
     }
     const uint32_t lds0 = lds_u32(&sm.ring[0]);
+    const uint32_t lds_asb = lds_u32(&sm.asb[0][0]), lds_asd = lds_u32(&sm.asdummy[0]);
     constexpr uint32_t SLOT = sizeof(Slot);
     constexpr uint32_t OFF_B = offsetof(Slot, b), OFF_AS = offsetof(Slot, as), OFF_BS = offsetof(Slot, bs);
 
@@ -170,6 +185,13 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
                 const bool ok = live && b_col[u] < p.n - col0;
                 const uint32_t wpart = (uint32_t)(kk + 4 * (4 * wave_u + u)) * (uint32_t)p.n + (uint32_t)col0;
                 load_lds16(rb, slot + OFF_B + (uint32_t)(4 * wave_u + u) * 1024u, ok ? b_lane[u] + wpart : kOOB);
+            } else if constexpr (d == 8 && AS8) {
+                // rows 64 wave + l: the 16 scale bytes of k blocks 16 (stage / 8) .. + 15 with
+                // the block's first slice, a placeholder load with the others
+                const bool real = live && (stage & 7) == 0;
+                const uint32_t off = (uint32_t)(64 * wave_u + l) * (uint32_t)kb + (uint32_t)(16 * (stage >> 3));
+                const uint32_t dst = (real ? lds_asb + (uint32_t)((stage >> 3) & 1) * AS8_BYTES : lds_asd) + (uint32_t)wave_u * 1024u;
+                load_lds16(rsa, dst, real ? off : kOOB);
             } else if constexpr (d == 8) {
                 // rows 64 wave + l: the 4 scale bytes of k blocks 4 (stage / 2) .. + 3
                 const uint32_t off = (uint32_t)(64 * wave_u + l) * (uint32_t)kb + (uint32_t)(4 * (stage >> 1));
@@ -208,7 +230,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
             wait_vm<PER * (STAGES - 2) + PER / 2>();   // slice 0 in LDS
             lds_barrier();
             if constexpr (NB > 0) {
-                static_for<0, NB>([&](auto i_c) { read_a(f, decltype(i_c)::value, sm.ring[0], r0w, 0); });
+                static_for<0, NB>([&](auto i_c) { read_a<AS8>(f, decltype(i_c)::value, sm.ring[0], sm, r0w, 0); });
                 read_b(f, 0, sm.ring[0], c0w, cp);
                 read_b(f, 1, sm.ring[0], c0w, cp);
             }
@@ -251,7 +273,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
                     if constexpr (NEXT) {
                         if constexpr (m == 0) read_b(f, 0, s, c0w, cp);
                         if constexpr (m == 2 || (NB == 1 && m == 1)) read_b(f, 1, s, c0w, cp);
-                        if constexpr (m & 1) read_a(f, m >> 1, s, r0w, ks1);
+                        if constexpr (m & 1) read_a<AS8>(f, m >> 1, s, sm, r0w, ks1);
                         // ring load q after MFMA q * NM / ND (several after the last when NM < ND)
                         static_for<0, ND>([&](auto q_c) {
                             constexpr int q = decltype(q_c)::value;
@@ -291,6 +313,9 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
 
 }  // namespace mx
 
+// row scales in blocks of 8 k slices: 16-byte loads of 16-byte aligned rows
+static bool as8_ok(const MParams& p) { return p.k % 512 == 0 && ((uintptr_t)p.lhs_scale & 15) == 0; }
+
 bool ragged_m_mx_fast_ok(const MParams& p) {
     // 16-byte ring loads of A and B, 4-byte loads of both scale arrays; 32-bit offsets
     const uint64_t w = (uint64_t)p.k * (uint64_t)p.n;
@@ -299,14 +324,20 @@ bool ragged_m_mx_fast_ok(const MParams& p) {
     return p.k % 128 == 0 && p.n % 16 == 0 && w + 64ull * p.n < (1ull << 31) && a < (1ull << 31) && o < (1ull << 31);
 }
 
-hipError_t launch_ragged_m_mx_fast(const MParams& p, int grid, hipStream_t s) {
+template <bool AS8>
+static void launch_mx(const MParams& p, int grid, hipStream_t s) {
     if (p.epi) {
-        if (p.out_f32) hipLaunchKernelGGL((mx::kernel<true, float>), dim3(grid), dim3(mx::NT), 0, s, p);
-        else hipLaunchKernelGGL((mx::kernel<true, uint16_t>), dim3(grid), dim3(mx::NT), 0, s, p);
+        if (p.out_f32) hipLaunchKernelGGL((mx::kernel<AS8, true, float>), dim3(grid), dim3(mx::NT), 0, s, p);
+        else hipLaunchKernelGGL((mx::kernel<AS8, true, uint16_t>), dim3(grid), dim3(mx::NT), 0, s, p);
     } else {
-        if (p.out_f32) hipLaunchKernelGGL((mx::kernel<false, float>), dim3(grid), dim3(mx::NT), 0, s, p);
-        else hipLaunchKernelGGL((mx::kernel<false, uint16_t>), dim3(grid), dim3(mx::NT), 0, s, p);
+        if (p.out_f32) hipLaunchKernelGGL((mx::kernel<AS8, false, float>), dim3(grid), dim3(mx::NT), 0, s, p);
+        else hipLaunchKernelGGL((mx::kernel<AS8, false, uint16_t>), dim3(grid), dim3(mx::NT), 0, s, p);
     }
+}
+
+hipError_t launch_ragged_m_mx_fast(const MParams& p, int grid, hipStream_t s) {
+    if (as8_ok(p)) launch_mx<true>(p, grid, s);
+    else launch_mx<false>(p, grid, s);
     return hipGetLastError();
 }
 

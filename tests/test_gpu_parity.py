@@ -180,6 +180,9 @@ MX_RING_CASES = [
     (520, 1024, 272, [520]),
     (257, 128, 256, [128, 129]),
     (96, 384, 512, [32, 0, 64]),
+    # row scales in blocks of 8 k slices (k % 512 == 0): five blocks, so both scale buffers
+    # are refilled, with a short group and partial row and column tiles
+    (400, 2560, 272, [3, 200, 0, 197]),
 ]
 
 
