@@ -233,6 +233,46 @@ def test_ragged_m_nk(case):
         check_fp32(y32, ref, "nk case 0, fp32 out")
 
 
+# ---- seeded random shapes on the ring paths ------------------------------------------------
+# bf16 with [g,k,n] weights, bf16 with [g,n,k] weights (k, n multiples of 8) and MXFP8 (k a
+# multiple of 128, n of 16): random slice counts (odd and even, k tails inside a slice),
+# random group sizes with empty groups, rows past the groups' total, ragged column tiles.
+
+def _random_case(i):
+    r = np.random.default_rng([4242, i])
+    kind = ("bf16", "nk", "mxfp8")[i % 3]
+    if kind == "mxfp8":
+        k = int(r.choice([128, 256, 384, 512, 640, 1024, 1536, 2048]))
+        n = int(16 * r.integers(1, 40))
+    else:
+        k = int(8 * r.integers(1, 200))
+        n = int(8 * r.integers(1, 80))
+    g = int(r.integers(1, 12))
+    gs = r.integers(0, 400, g)
+    gs[r.random(g) < 0.2] = 0
+    m = max(1, int(gs.sum() + r.integers(0, 50)))
+    return kind, m, k, n, gs.astype(np.int32)
+
+
+@pytest.mark.parametrize("i", range(36))
+def test_ragged_m_random_shapes(i):
+    kind, m, k, n, gs = _random_case(i)
+    say("ragged_m random", kind, m, k, n, gs.tolist())
+    d = to_dev(W.small_inputs("m", "mxfp8" if kind == "mxfp8" else "bf16", m, k, n, gs, seed=500 + i))
+    out = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    if kind == "nk":
+        rhs_nk = d["rhs"].transpose(1, 2).contiguous()
+        ref = oracle.ragged_dot_m_nk(raw(d["lhs"]), raw(rhs_nk), raw(d["group_sizes"]))
+        y = gg().ragged_dot_m(d["lhs"], rhs_nk, d["group_sizes"], out=out, rhs_layout="nk")
+    else:
+        ref = oracle_m(d)
+        y = gg().ragged_dot_m(d["lhs"], d["rhs"], d["group_sizes"], out=out, lhs_scale=d.get("lhs_scale"),
+                              rhs_scale=d.get("rhs_scale"))
+    torch.cuda.synchronize()
+    check_bf16(y, ref, f"random case {i} ({kind})")
+    assert torch.all(y[int(gs.sum()):] == 0)
+
+
 # ---- fused gate/up projection: act(x . w0 + b0) * (x . w1 + b1) ------------------------------
 
 GATED_CASES = [
