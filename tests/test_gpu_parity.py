@@ -273,6 +273,50 @@ def test_ragged_m_random_shapes(i):
     assert torch.all(y[int(gs.sum()):] == 0)
 
 
+@pytest.mark.parametrize("i", range(12))
+def test_ragged_k_random_shapes(i):
+    """The contracting ring kernel on seeded random shapes: groups of 0 to 700 rows (row
+    slices of 32 with tails), k and n multiples of 8 with ragged output tiles."""
+    r = np.random.default_rng([4343, i])
+    g = int(r.integers(1, 10))
+    gs = r.integers(0, 700, g).astype(np.int32)
+    gs[r.random(g) < 0.2] = 0
+    m = max(1, int(gs.sum() + r.integers(0, 40)))
+    k, n = int(8 * r.integers(1, 90)), int(8 * r.integers(1, 90))
+    say("ragged_k random", m, k, n, gs.tolist())
+    d = to_dev(W.small_inputs("k", "bf16", m, k, n, gs, seed=600 + i))
+    out = torch.full((g, k, n), float("nan"), dtype=torch.float32, device=DEV)
+    y = gg().ragged_dot_k(d["lhs"], d["dout"], d["group_sizes"], out=out)
+    torch.cuda.synchronize()
+    ref = oracle.ragged_dot_k(raw(d["lhs"]), raw(d["dout"]), raw(d["group_sizes"]))
+    for h, sz in enumerate(gs):
+        if sz == 0:
+            assert torch.all(y[h] == 0), f"random k case {i}: empty group {h}"
+    if np.any(ref != 0):
+        check_fp32(y, ref, f"random k case {i}")
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_ragged_m_gated_random_shapes(i):
+    """The gated ring kernel on seeded random shapes (k, n multiples of 8), without biases."""
+    r = np.random.default_rng([4444, i])
+    g = int(r.integers(1, 8))
+    gs = r.integers(0, 400, g).astype(np.int32)
+    gs[r.random(g) < 0.2] = 0
+    m = max(1, int(gs.sum() + r.integers(0, 40)))
+    k, n = int(8 * r.integers(1, 120)), int(8 * r.integers(1, 60))
+    act = ("silu", "gelu_tanh")[i % 2]
+    say("ragged_m_gated random", m, k, n, gs.tolist(), act)
+    d = to_dev(W.small_inputs("m", "bf16", m, k, n, gs, seed=700 + i))
+    w1 = to_dev(W.small_inputs("m", "bf16", m, k, n, gs, seed=750 + i))["rhs"]
+    ref = oracle.ragged_dot_m_gated(raw(d["lhs"]), raw(d["rhs"]), raw(w1), gs, act=act)
+    out = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    y = gg().ragged_dot_m_gated(d["lhs"], d["rhs"], w1, d["group_sizes"], act=act, out=out)
+    torch.cuda.synchronize()
+    check_bf16(y, ref, f"random gated case {i}")
+    assert torch.all(y[int(gs.sum()):] == 0)
+
+
 # ---- fused gate/up projection: act(x . w0 + b0) * (x . w1 + b1) ------------------------------
 
 GATED_CASES = [
