@@ -244,6 +244,32 @@ def padded_dot_m(lhs, rhs, group_sizes, capacity, lhs_scale=None, rhs_scale=None
     return out
 
 
+def padded_dot_k(lhs, dout, group_sizes, capacity):
+    """The padded contracting form written as its steps, in fp64 numpy:
+    (1) scatter the rows of group g of lhs and of dout into slabs P[g, 0:m_g] of zeroed
+    [g, C, k] and [g, C, n] buffers;
+    (2) one batched product P_lhs[g]^T @ P_dout[g] -> [g, k, n].
+    Rows past a group's capacity are dropped (only the first C rows of the group are
+    scattered), as are rows past sum(group_sizes) -- the clamping reading of the ragged
+    oracle.  ("Group-GEMM in XLA", Part 1 "The Naive Support, and Why It Hurts:
+    Padded-Dot", applied to the contracting variant of Part 3 "Contracting".)"""
+    gs = np.asarray(group_sizes, dtype=np.int64)
+    m, k = lhs.shape
+    n = dout.shape[1]
+    g = gs.shape[0]
+    A, D = decode(lhs), decode(dout)
+    PA = np.zeros((g, capacity, k))
+    PD = np.zeros((g, capacity, n))
+    covered = 0
+    for h in range(g):
+        s = min(max(int(gs[h]), 0), m - covered)
+        c = min(s, capacity)
+        PA[h, :c] = A[covered:covered + c]
+        PD[h, :c] = D[covered:covered + c]
+        covered += s
+    return np.matmul(np.swapaxes(PA, 1, 2), PD)   # step 2: uniform batched contraction
+
+
 def bf16_values(a):
     """fp64 values of bfloat16 bit patterns (uint16): a bfloat16 is the upper half of an
     IEEE binary32, so the pattern shifted up 16 bits is that binary32 exactly."""

@@ -127,6 +127,55 @@ def test_padded_equals_ragged(capacity):
     np.testing.assert_allclose(padded, ragged, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("gs,m,cap", [([5, 0, 4], 9, 3), ([2, 6, 1], 10, 4), ([7], 7, 1), ([0, 3, 3], 8, 3)])
+def test_padded_m_over_capacity_brute_force(gs, m, cap):
+    """Rows past a group's capacity are dropped: the first min(m_g, C) rows of every group
+    get their product, the rest of the group and rows past sum(group_sizes) are 0 (written
+    out with plain loops; keeping any other C rows of a group fails here)."""
+    k, n = 3, 4
+    r = np.random.default_rng(16)
+    lhs, rhs = _f32(r.standard_normal((m, k))), _f32(r.standard_normal((len(gs), k, n)))
+    out = oracle.padded_dot_m(lhs, rhs, gs, cap)
+    expect = np.zeros((m, n))
+    row = 0
+    for h, s in enumerate(gs):
+        for i in range(s):
+            if i < cap:
+                for j in range(n):
+                    expect[row, j] = sum(float(lhs[row, t]) * float(rhs[h, t, j]) for t in range(k))
+            row += 1
+    np.testing.assert_allclose(out, expect, rtol=1e-14, atol=1e-14)
+    assert np.count_nonzero(np.any(out != 0, axis=1)) == sum(min(s, cap) for s in gs)
+
+
+@pytest.mark.parametrize("capacity", ["max", "m"])
+def test_padded_k_equals_ragged(capacity):
+    m, k, n, gs = 24, 6, 5, [6, 0, 11, 3, 4]
+    r = np.random.default_rng(17)
+    lhs, dout = _f32(r.standard_normal((m, k))), _f32(r.standard_normal((m, n)))
+    C = max(gs) if capacity == "max" else m
+    np.testing.assert_allclose(oracle.padded_dot_k(lhs, dout, gs, C), oracle.ragged_dot_k(lhs, dout, gs),
+                               rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("gs,m,cap", [([5, 0, 4], 9, 3), ([2, 6, 1], 10, 4)])
+def test_padded_k_over_capacity_brute_force(gs, m, cap):
+    """The contracting padded form over capacity: group h sums over its first min(m_h, C)
+    rows only (plain loops)."""
+    k, n = 3, 4
+    r = np.random.default_rng(18)
+    lhs, dout = _f32(r.standard_normal((m, k))), _f32(r.standard_normal((m, n)))
+    out = oracle.padded_dot_k(lhs, dout, gs, cap)
+    expect = np.zeros((len(gs), k, n))
+    start = 0
+    for h, s in enumerate(gs):
+        for i in range(k):
+            for j in range(n):
+                expect[h, i, j] = sum(float(lhs[start + q, i]) * float(dout[start + q, j]) for q in range(min(s, cap)))
+        start += s
+    np.testing.assert_allclose(out, expect, rtol=1e-14, atol=1e-14)
+
+
 # ---- P6: brute force on tiny shapes, boundary cases ---------------------------------------
 
 @pytest.mark.parametrize("gs,m", [([0, 0, 0], 5), ([5, 0, 0], 5), ([0, 5, 0], 5), ([0, 0, 5], 5),
@@ -278,6 +327,26 @@ def test_k_epilogue_beta_is_gradient_accumulation():
         s1 += gs1[h]; s2 += gs2[h]
     union = oracle.ragged_dot_k(np.concatenate(rows_a), np.concatenate(rows_d), [a + b for a, b in zip(gs1, gs2)])
     np.testing.assert_allclose(acc, union, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("alpha,beta", [(-2.0, 0.25), (0.5, 1.0), (3.0, 0.0), (1.0, -0.5)])
+def test_k_epilogue_alpha_beta_brute_force(alpha, beta):
+    """out[h] = alpha * (sum over the rows of h of lhs^T dout) + beta * c[h], written out with
+    plain loops; an empty group gives exactly beta * c[h].  alpha scales the product only:
+    alpha * (acc + beta * c) fails here whenever alpha != 1 and beta != 0."""
+    m, k, n, gs = 8, 3, 4, [3, 0, 5]
+    r = np.random.default_rng(19)
+    lhs, dout = _f32(r.standard_normal((m, k))), _f32(r.standard_normal((m, n)))
+    c = r.standard_normal((len(gs), k, n))
+    out = oracle.ragged_dot_k_epilogue(lhs, dout, gs, alpha=alpha, beta=beta, c=c)
+    start = 0
+    for h, s in enumerate(gs):
+        for i in range(k):
+            for j in range(n):
+                acc = sum(float(lhs[start + q, i]) * float(dout[start + q, j]) for q in range(s))
+                assert math.isclose(out[h, i, j], alpha * acc + beta * c[h, i, j], rel_tol=1e-13, abs_tol=1e-13)
+        start += s
+    assert np.array_equal(out[1], beta * c[1])
 
 
 def test_activations_match_library_routines():
