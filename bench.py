@@ -1,18 +1,21 @@
 """Benchmark of the ragged-dot Group-GEMM on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME|all] [--no-cpu-baseline]
 
 A step is one ragged-dot call over one batch of synthetic routed-token input already
 resident in HBM (the whole hot path: group_sizes scan, tile schedule, MFMA main loop,
-masked tails, epilogue -- one kernel launch).  The default workload is the Mixtral-8x7B-
+masked tails, epilogue -- one kernel launch).  The headline workload is the Mixtral-8x7B-
 like FFN up-projection: 4096 tokens, top-2 of 8 experts (m = 8192 rows), k = 4096,
 n = 14336, bf16 in / fp32 accumulate / bf16 out.  The timing protocol follows the pages'
-micro-benchmark (10 warm-up runs, then timed runs).
+micro-benchmark (10 warm-up runs, then timed runs; per-launch median and mean from HIP
+events on the launch stream).
 
-Prints one JSON line: useful TFLOP/s (2 * sum(group_sizes) * k * n per step), the
-roofline of the kernel (from HIP events on the launch stream), the speedup over the
-capacity-padded baseline on the same inputs, and the CPU oracle timed on a bounded
-sample of the same workload.
+Prints one JSON line: useful TFLOP/s of the headline workload (2 * sum(group_sizes) * k * n
+per step), the roofline of its kernel, the speedup over the capacity-padded baseline on the
+same inputs, and the CPU oracle timed on a bounded sample of the same workload.  With the
+default ``--workload all`` the line also carries ``per_config``: the same figures for each of
+the five workloads (the 64-row fp32 one, the Mixtral-like bf16 forward, the DeepSeek-like
+skewed forward, the Mixtral-like MXFP8 forward and the Llama-4-Scout-like weight gradient).
 """
 import argparse
 import json
@@ -29,6 +32,9 @@ PEAK_HBM_GBS = 8000.0
 
 METRIC = "ragged-dot useful TFLOP/s + % MFMA/HBM roofline; speedup vs padded dot"
 DEFAULT_WORKLOAD = "mixtral8x7b_up_bf16"
+# the five workloads the benchmark reports together (the headline is the second)
+PER_CONFIG = ["tiny_fp32", "mixtral8x7b_up_bf16", "deepseekv3_routed_bf16", "mixtral8x7b_up_mxfp8",
+              "llama4scout_wgrad_bf16"]
 PROFILE_TRAFFIC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
 
 
@@ -37,7 +43,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default="all",
+                    help="a workload name, or 'all' (the headline plus every entry of PER_CONFIG)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-padded", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -80,20 +87,33 @@ def useful_flops(w, gs):
 
 def time_calls(fn, steps, warmup, torch):
     """Wall time of `steps` calls (after `warmup`), synchronised on both sides, and the
-    per-launch time from HIP events recorded on the launch stream."""
+    per-launch times from a HIP event pair around every call, recorded on the launch
+    stream (the library enqueues on torch's current stream)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(steps):
+    for e0, e1 in evs:
+        e0.record(stream)
         fn()
-    ev1.record(stream)
+        e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, ev0.elapsed_time(ev1) / 1e3 / steps
+    per = np.array([e0.elapsed_time(e1) / 1e3 for e0, e1 in evs])
+    return wall, per
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(w, d, gs, target_s, W, torch):
@@ -143,7 +163,29 @@ def cpu_baseline(w, d, gs, target_s, W, torch):
         if dt < target_s / 4:
             cnt *= 2
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(oracle.num_threads()), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{done} {unit} of the {w.name} workload drawn uniformly, fp64 oracle, {spent:.1f} s"}
+
+
+def cpu_whole_call(w, d, W, threads):
+    """The oracle's whole call on a workload small enough to finish in milliseconds, at a
+    given thread count; seconds per call (median of repeated calls over ~1 s)."""
+    import oracle
+    raw = W.to_numpy_raw
+    lhs, rhs, gsn = raw(d["lhs"]), raw(d["rhs"]), raw(d["group_sizes"])
+    before = oracle.num_threads()
+    oracle.set_num_threads(threads)
+    try:
+        times, spent = [], 0.0
+        while spent < 1.0 or len(times) < 5:
+            t0 = time.perf_counter()
+            oracle.ragged_dot_m(lhs, rhs, gsn)
+            dt = time.perf_counter() - t0
+            times.append(dt)
+            spent += dt
+    finally:
+        oracle.set_num_threads(before)
+    return float(np.median(times))
 
 
 def cpu_baseline_routing(w, d, target_s, raw, oracle):
@@ -245,6 +287,113 @@ def ingest_traffic(a):
         f.write("\n")
 
 
+def make_call(w, d, G, torch, dev):
+    """The timed call of a workload (outputs and workspace allocated once, outside it)."""
+    if w.op == "permute":
+        ws = torch.empty(G.workspace_bytes("permute", w.m, w.k, 0, w.g), dtype=torch.uint8, device=dev)
+        outs = G.moe_permute(d["x"], d["experts"], w.g, workspace=ws)
+        return lambda: G.moe_permute(d["x"], d["experts"], w.g, workspace=ws, out=outs), None
+    if w.op == "unpermute":
+        # the inverse order the permute of the same routing produces (narrow rows: only the
+        # index maps are used)
+        narrow = torch.zeros((w.tokens, 8), dtype=torch.bfloat16, device=dev)
+        c2s = G.moe_permute(narrow, d["experts"], w.g)[4]
+        out = torch.empty((w.tokens, w.n), dtype=torch.bfloat16, device=dev)
+        return lambda: G.moe_unpermute(d["y"], c2s, d["weights"], out=out), out
+    if w.op == "m_gated":
+        out = torch.empty((w.m, w.n), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(G.workspace_bytes("ragged_m", w.m, w.k, w.n, w.g), dtype=torch.uint8, device=dev)
+        return lambda: G.ragged_dot_m_gated(d["lhs"], d["w0"], d["w1"], d["group_sizes"], act="silu", out=out,
+                                            workspace=ws), out
+    if w.op in ("m", "m_nk"):
+        out_dtype = torch.float32 if w.out_dtype == "f32" else torch.bfloat16
+        out = torch.empty((w.m, w.n), dtype=out_dtype, device=dev)
+        ws = torch.empty(G.workspace_bytes("ragged_m", w.m, w.k, w.n, w.g), dtype=torch.uint8, device=dev)
+        layout = "nk" if w.op == "m_nk" else "kn"
+        return lambda: G.ragged_dot_m(d["lhs"], d["rhs"], d["group_sizes"], out=out, lhs_scale=d.get("lhs_scale"),
+                                      rhs_scale=d.get("rhs_scale"), workspace=ws, rhs_layout=layout), out
+    out = torch.empty((w.g, w.k, w.n), dtype=torch.float32, device=dev)
+    ws = torch.empty(G.workspace_bytes("ragged_k", w.m, w.k, w.n, w.g), dtype=torch.uint8, device=dev)
+    return lambda: G.ragged_dot_k(d["lhs"], d["dout"], d["group_sizes"], out=out, workspace=ws), out
+
+
+def run_workload(name, a, torch, G, W, dev, cpu=True):
+    """Times one workload; returns its record (the fields of the JSON line's `config`,
+    `roofline`, `padded` and `cpu_baseline`, plus the value and step time)."""
+    w = W.WORKLOADS[name]
+    gs = W.group_sizes(w)
+    d = W.make_inputs(w, device=dev, gs=gs)
+    torch.cuda.synchronize()
+    F = useful_flops(w, gs)
+    B = algorithmic_bytes(w, gs)
+    fn, out = make_call(w, d, G, torch, dev)
+    wall, per = time_calls(fn, a.steps, a.warmup, torch)
+    ms_per_step = wall / a.steps * 1e3
+    med, mean = float(np.median(per)), float(np.mean(per))
+    routing = w.op in ("permute", "unpermute")
+    # pure data movement is rated in GB/s of algorithmic bytes, the products in TFLOP/s
+    value = B / (wall / a.steps) / 1e9 if routing else F / (wall / a.steps) / 1e12
+
+    # roofline of the (single) kernel: MFMA-bound if the arithmetic intensity exceeds the
+    # ridge point of its precision, else HBM-bound; achieved over the median launch
+    peak_f = PEAK_TFLOPS[w.in_dtype]
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if not routing and F / B >= ridge:
+        roof = {"bound": "mfma", "achieved": F / med / 1e12, "peak": peak_f, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": B / med / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_for(w.name)
+
+    config = {"workload": w.name, "op": f"moe_{w.op}" if routing else f"ragged_dot_{w.op}", "m": w.m, "k": w.k,
+              "n": w.n, "g": w.g,
+              "group_sizes": {"min": int(gs.min()), "max": int(gs.max()), "sum": int(gs.sum()),
+                              "empty": int((gs == 0).sum())},
+              "useful_gflop_per_step": F / 1e9, "algorithmic_mb_per_step": B / 1e6,
+              "kernel_us_per_launch": {"median": med * 1e6, "mean": mean * 1e6, "min": float(per.min()) * 1e6}}
+    if routing:
+        config["tokens"], config["top_k"] = w.tokens, w.top_k
+        if w.op == "permute":
+            config["kernels"] = "histogram, rank, gather (one call; roofline over the whole call)"
+    padded = None
+    if not a.no_padded and not routing and w.op not in ("m_nk", "m_gated"):
+        cap = int(math.ceil(gs.max() / 256.0) * 256)
+        pws = torch.empty(G.workspace_bytes(f"padded_{w.op}", w.m, w.k, w.n, w.g, cap, d["lhs"].dtype),
+                          dtype=torch.uint8, device=dev)
+        if w.op == "m":
+            pfn = lambda: G.padded_dot("m", d["lhs"], d["rhs"], d["group_sizes"], cap, out=out,
+                                       a_scale=d.get("lhs_scale"), b_scale=d.get("rhs_scale"), workspace=pws)
+        else:
+            pfn = lambda: G.padded_dot("k", d["lhs"], d["dout"], d["group_sizes"], cap, out=out, workspace=pws)
+        psteps = max(5, a.steps // 2)
+        pwall, pper = time_calls(pfn, psteps, max(2, a.warmup // 2), torch)
+        pmed = float(np.median(pper))
+        padded = {"capacity": cap, "capacity_rule": "largest group rounded up to 256 rows",
+                  "ms_per_step": pwall / psteps * 1e3, "us_per_call_median": pmed * 1e6,
+                  "useful_tflops": F / pmed / 1e12, "speedup_ragged_vs_padded": pmed / med}
+        del pws
+    elif w.op in ("m_nk", "m_gated"):
+        padded = None   # padded_dot is the plain [g,k,n] product only
+    rec = {"value": value, "unit": "GB/s" if routing else "TFLOP/s", "ms_per_step": ms_per_step,
+           "dtype": {"bf16": "bf16", "f32": "f32", "mxfp8": "e4m3"}[w.in_dtype], "config": config, "roofline": roof,
+           "padded": padded}
+    if cpu and not a.no_cpu_baseline:
+        if w.name == "tiny_fp32":
+            # small enough for whole oracle calls: all host threads and one thread
+            import oracle
+            t_all = cpu_whole_call(w, d, W, oracle.num_threads())
+            t_one = cpu_whole_call(w, d, W, 1)
+            rec["cpu_baseline"] = {"value": F / t_all / 1e12, "unit": "TFLOP/s", "cores": int(oracle.num_threads()),
+                                   "kind": "oracle", "cpu_model": cpu_model(),
+                                   "sample": "whole calls, median", "us_per_call": t_all * 1e6,
+                                   "us_per_call_1_thread": t_one * 1e6}
+        else:
+            rec["cpu_baseline"] = cpu_baseline(w, d, gs, a.cpu_seconds, W, torch)
+    del d, fn, out
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     a = parse()
     if a.traffic_from:
@@ -267,93 +416,35 @@ def main():
     from group_gemm_amd import workloads as W
 
     G.lib()   # fail loudly if the HIP library is missing
-    w = W.WORKLOADS[a.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    gs = W.group_sizes(w)
-    d = W.make_inputs(w, device=dev, gs=gs)
-    torch.cuda.synchronize()
-    F = useful_flops(w, gs)
-    B = algorithmic_bytes(w, gs)
-
-    if w.op == "permute":
-        ws = torch.empty(G.workspace_bytes("permute", w.m, w.k, 0, w.g), dtype=torch.uint8, device=dev)
-        outs = G.moe_permute(d["x"], d["experts"], w.g, workspace=ws)
-        fn = lambda: G.moe_permute(d["x"], d["experts"], w.g, workspace=ws, out=outs)
-    elif w.op == "unpermute":
-        # the inverse order the permute of the same routing produces (narrow rows: only the
-        # index maps are used)
-        narrow = torch.zeros((w.tokens, 8), dtype=torch.bfloat16, device=dev)
-        c2s = G.moe_permute(narrow, d["experts"], w.g)[4]
-        out = torch.empty((w.tokens, w.n), dtype=torch.bfloat16, device=dev)
-        fn = lambda: G.moe_unpermute(d["y"], c2s, d["weights"], out=out)
-    elif w.op == "m_gated":
-        out = torch.empty((w.m, w.n), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(G.workspace_bytes("ragged_m", w.m, w.k, w.n, w.g), dtype=torch.uint8, device=dev)
-        fn = lambda: G.ragged_dot_m_gated(d["lhs"], d["w0"], d["w1"], d["group_sizes"], act="silu", out=out, workspace=ws)
-    elif w.op in ("m", "m_nk"):
-        out_dtype = torch.float32 if w.out_dtype == "f32" else torch.bfloat16
-        out = torch.empty((w.m, w.n), dtype=out_dtype, device=dev)
-        ws = torch.empty(G.workspace_bytes("ragged_m", w.m, w.k, w.n, w.g), dtype=torch.uint8, device=dev)
-        layout = "nk" if w.op == "m_nk" else "kn"
-        fn = lambda: G.ragged_dot_m(d["lhs"], d["rhs"], d["group_sizes"], out=out, lhs_scale=d.get("lhs_scale"),
-                                    rhs_scale=d.get("rhs_scale"), workspace=ws, rhs_layout=layout)
+    headline = DEFAULT_WORKLOAD if a.workload == "all" else a.workload
+    if headline not in W.WORKLOADS:
+        raise SystemExit(f"unknown workload {headline!r}; known: {sorted(W.WORKLOADS)}")
+    per_config = {}
+    if a.workload == "all":
+        for name in PER_CONFIG:
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            per_config[name] = run_workload(name, a, torch, G, W, dev)
+        rec = per_config[headline]
     else:
-        out = torch.empty((w.g, w.k, w.n), dtype=torch.float32, device=dev)
-        ws = torch.empty(G.workspace_bytes("ragged_k", w.m, w.k, w.n, w.g), dtype=torch.uint8, device=dev)
-        fn = lambda: G.ragged_dot_k(d["lhs"], d["dout"], d["group_sizes"], out=out, workspace=ws)
-
-    wall, per_launch = time_calls(fn, a.steps, a.warmup, torch)
-    ms_per_step = wall / a.steps * 1e3
-    routing = w.op in ("permute", "unpermute")
-    # pure data movement is rated in GB/s of algorithmic bytes, the products in TFLOP/s
-    value = B / (wall / a.steps) / 1e9 if routing else F / (wall / a.steps) / 1e12
-
-    # roofline of the (single) kernel: MFMA-bound if the arithmetic intensity exceeds the
-    # ridge point of its precision, else HBM-bound
-    peak_f = PEAK_TFLOPS[w.in_dtype]
-    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
-    if not routing and F / B >= ridge:
-        roof = {"bound": "mfma", "achieved": F / per_launch / 1e12, "peak": peak_f, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": B / per_launch / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_for(w.name)
-
-    config = {"workload": w.name, "op": f"moe_{w.op}" if routing else f"ragged_dot_{w.op}", "m": w.m, "k": w.k,
-              "n": w.n, "g": w.g,
-              "group_sizes": {"min": int(gs.min()), "max": int(gs.max()), "sum": int(gs.sum()),
-                              "empty": int((gs == 0).sum())},
-              "useful_gflop_per_step": F / 1e9, "algorithmic_mb_per_step": B / 1e6,
-              "kernel_us_per_launch": per_launch * 1e6}
-
-    if routing:
-        config["tokens"], config["top_k"] = w.tokens, w.top_k
-        if w.op == "permute":
-            config["kernels"] = "histogram, rank, gather (one call; roofline over the whole call)"
-    elif not a.no_padded and w.op in ("m_nk", "m_gated"):
-        config["padded"] = None   # padded_dot is the plain [g,k,n] product only
-    elif not a.no_padded:
-        cap = int(math.ceil(gs.max() / 256.0) * 256)
-        pws = torch.empty(G.workspace_bytes(f"padded_{w.op}", w.m, w.k, w.n, w.g, cap, d["lhs"].dtype),
-                          dtype=torch.uint8, device=dev)
-        if w.op == "m":
-            pfn = lambda: G.padded_dot("m", d["lhs"], d["rhs"], d["group_sizes"], cap, out=out,
-                                       a_scale=d.get("lhs_scale"), b_scale=d.get("rhs_scale"), workspace=pws)
-        else:
-            pfn = lambda: G.padded_dot("k", d["lhs"], d["dout"], d["group_sizes"], cap, out=out, workspace=pws)
-        pwall, _ = time_calls(pfn, max(5, a.steps // 2), max(2, a.warmup // 2), torch)
-        p_ms = pwall / max(5, a.steps // 2) * 1e3
-        config["padded"] = {"capacity": cap, "ms_per_step": p_ms, "useful_tflops": F / (p_ms / 1e3) / 1e12,
-                            "speedup_ragged_vs_padded": p_ms / ms_per_step}
-        del pws
-
-    line = {"metric": METRIC, "value": value, "unit": "GB/s" if routing else "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-            "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": {"bf16": "bf16", "f32": "f32", "mxfp8": "e4m3"}[w.in_dtype],
-            "data": "synthetic (seeded routing and N(0,1) / N(0,1/k) operands)", "config": config, "roofline": roof}
-    if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, d, gs, a.cpu_seconds, W, torch)
+        rec = run_workload(headline, a, torch, G, W, dev)
+    config = dict(rec["config"])
+    config["padded"] = rec["padded"]
+    line = {"metric": METRIC, "value": rec["value"], "unit": rec["unit"], "n_gpus": 1, "steps": a.steps,
+            "warmup": a.warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": rec["dtype"],
+            "data": "synthetic (seeded routing and N(0,1) / N(0,1/k) operands)", "config": config,
+            "roofline": rec["roofline"]}
+    if "cpu_baseline" in rec:
+        line["cpu_baseline"] = rec["cpu_baseline"]
+    if per_config:
+        line["per_config"] = {name: {"value": r["value"], "unit": r["unit"], "dtype": r["dtype"],
+                                     "us_per_launch": r["config"]["kernel_us_per_launch"],
+                                     "config": {k: v for k, v in r["config"].items() if k != "kernel_us_per_launch"},
+                                     "roofline": r["roofline"], "padded": r["padded"],
+                                     "cpu_baseline": r.get("cpu_baseline")}
+                              for name, r in per_config.items()}
     print(json.dumps(line), flush=True)
 
 

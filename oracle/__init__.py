@@ -336,3 +336,10 @@ def moe_unpermute(y, copy_to_sorted, weights):
 
 def num_threads():
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n):
+    """Thread count of the C oracle's later calls (OpenMP)."""
+    L = lib()
+    L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    L.oracle_set_num_threads(int(n))

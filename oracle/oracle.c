@@ -194,3 +194,13 @@ int oracle_num_threads(void) {
     return 1;
 #endif
 }
+
+/* sets the OpenMP thread count of later calls (the benchmark times a one-thread run) */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

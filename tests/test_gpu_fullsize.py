@@ -2,8 +2,9 @@
 
 The oracle cannot recompute a whole [32768, 2048] or [16, 5120, 8192] result in test
 time, so it checks sampled outputs one by one: in the non-contracting form, the first and
-last row of sampled groups (group edges are where a wrong offset shows) plus random rows;
-in the contracting form, sampled (group, k-index) rows including both ends of k.  Every
+last row of every group (group edges are where a wrong offset shows), one row in every
+256-row tile of every group and random rows; in the contracting form, both ends of k and
+one k-index in every 256-wide k-tile of every group.  Every
 element of the result is also checked for properties that hold at any size: finite, and
 exactly zero past sum(group_sizes).
 """
@@ -26,14 +27,17 @@ def raw(t):
     return W.to_numpy_raw(t)
 
 
-def sample_rows(gs, rng, groups=48, extra=64):
+def sample_rows(gs, rng, extra=64, tile=256):
+    """The first and last row of every non-empty group, one random row in every 256-row
+    m-tile of every group (so every output tile the kernel computes is compared on at
+    least one row, over all of its columns), plus `extra` random rows."""
     starts = np.concatenate([[0], np.cumsum(gs)[:-1]])
-    nonempty = np.nonzero(gs)[0]
-    pick = set(rng.choice(nonempty, min(groups, nonempty.size), replace=False).tolist())
-    pick |= {int(np.argmax(gs)), int(nonempty[np.argmin(gs[nonempty])])}
     rows = []
-    for h in sorted(pick):
-        rows += [starts[h], starts[h] + gs[h] - 1, starts[h] + rng.integers(0, gs[h])]
+    for h in np.nonzero(gs)[0]:
+        st, s = int(starts[h]), int(gs[h])
+        rows += [st, st + s - 1]
+        for t0 in range(0, s, tile):
+            rows.append(st + t0 + int(rng.integers(0, min(tile, s - t0))))
     rows += rng.integers(0, int(gs.sum()), extra).tolist()
     return np.unique(np.array(rows, dtype=np.int64))
 
@@ -55,8 +59,8 @@ def test_full_size_ragged_m(name):
     if S < w.m:
         assert bool((out[S:] == 0).all())
     rng = np.random.default_rng(w.wid)
-    # the MXFP8 oracle decodes two scales per product: sample fewer rows for it
-    rows = sample_rows(gs, rng, groups=8, extra=8) if w.in_dtype == "mxfp8" else sample_rows(gs, rng)
+    # the MXFP8 oracle decodes two scales per product: fewer extra rows for it
+    rows = sample_rows(gs, rng, extra=8 if w.in_dtype == "mxfp8" else 64)
     ref = oracle.ragged_dot_m(raw(d["lhs"]), raw(d["rhs"]), gs, raw(d["lhs_scale"]) if "lhs_scale" in d else None,
                               raw(d["rhs_scale"]) if "rhs_scale" in d else None, rows=rows)
     y = out[torch.from_numpy(rows).to(DEV)].double().cpu().numpy()
@@ -110,11 +114,12 @@ def test_full_size_ragged_k():
     G.ragged_dot_k(d["lhs"], d["dout"], d["group_sizes"], out=out)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out).all()), "non-finite output"
+    # both ends of k and one k-index in every 256-wide k-tile, for every group
     rng = np.random.default_rng(5)
     pairs = []
     for h in range(w.g):
-        for i in [0, w.k - 1, int(rng.integers(0, w.k)), int(rng.integers(0, w.k))]:
-            pairs.append((h, i))
+        ks = {0, w.k - 1} | {t0 + int(rng.integers(0, min(256, w.k - t0))) for t0 in range(0, w.k, 256)}
+        pairs += [(h, i) for i in sorted(ks)]
     pairs = np.array(pairs, dtype=np.int64)
     ref = oracle.ragged_dot_k(raw(d["lhs"]), raw(d["dout"]), gs, pairs=pairs)
     y = out[torch.from_numpy(pairs[:, 0]).to(DEV), torch.from_numpy(pairs[:, 1]).to(DEV)].double().cpu().numpy()
