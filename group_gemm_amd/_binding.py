@@ -36,6 +36,8 @@ def lib():
         L.gg_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i32, i64, ctypes.c_int]
         L.gg_workspace_bytes.restype = sz
         L.ragged_dot_m.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
+        L.ragged_dot_m_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp,
+                                           vp]
         L.ragged_dot_k.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, ctypes.c_int, vp, sz, vp]
         L.ragged_dot_m_nk.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_int, ctypes.c_int, vp, sz, vp]
         f32 = ctypes.c_float
@@ -54,7 +56,7 @@ def lib():
         L.gg_status_string.argtypes = [ctypes.c_int]
         L.gg_status_string.restype = ctypes.c_char_p
         L.gg_abi_version.restype = ctypes.c_int
-        for f in ("ragged_dot_m", "ragged_dot_m_nk", "ragged_dot_m_epilogue", "ragged_dot_m_gated", "ragged_dot_k",
+        for f in ("ragged_dot_m", "ragged_dot_m_noalloc", "ragged_dot_m_nk", "ragged_dot_m_epilogue", "ragged_dot_m_gated", "ragged_dot_k",
                   "ragged_dot_k_epilogue",
                   "padded_dot", "moe_permute", "moe_unpermute", "gg_schedule", "gg_read_device_status"):
             getattr(L, f).restype = ctypes.c_int
@@ -208,6 +210,32 @@ def ragged_dot_m(lhs, rhs, group_sizes, out=None, out_dtype=None, lhs_scale=None
     code = lib().ragged_dot_m(_p(lhs), _p(rhs), _p(group_sizes), _p(out), m, k, n, g, GG_DT[lhs.dtype],
                               GG_DT[out.dtype], _p(lhs_scale), _p(rhs_scale), _p(ws), ws.numel(), _stream(dev))
     _check(code, "ragged_dot_m")
+    return out
+
+
+def ragged_dot_m_noalloc(lhs, rhs, group_sizes, out, lhs_scale=None, rhs_scale=None, status=None):
+    """ragged_dot_m into a caller-given `out` with no workspace: the library keeps the per-call
+    state in its own static device array (one per GPU; calls on one GPU must not overlap).
+    `status`: optional device int32 [1] that receives the GG_DEV_* bits.  Allocates nothing."""
+    dev = lhs.device
+    _tensor(lhs, "lhs", None, dtypes=_IN_DTYPES)
+    if lhs.dim() != 2 or rhs.dim() != 3:
+        raise ValueError("lhs must be [m,k] and rhs [g,k,n]")
+    m, k = lhs.shape
+    g, k2, n = rhs.shape
+    _tensor(rhs, "rhs", dev, dtype=lhs.dtype)
+    _tensor(group_sizes, "group_sizes", dev, (g,), torch.int32)
+    if k2 != k:
+        raise ValueError(f"lhs has k = {k}, rhs has {k2}")
+    _scales(lhs, lhs_scale, rhs_scale, m, k, n, g, dev)
+    if out is None:
+        raise ValueError("out must be given (the call allocates nothing)")
+    _out(out, "out", dev, (m, n), None)
+    if status is not None:
+        _tensor(status, "status", dev, (1,), dtypes=(torch.int32, torch.uint32))
+    code = lib().ragged_dot_m_noalloc(_p(lhs), _p(rhs), _p(group_sizes), _p(out), m, k, n, g, GG_DT[lhs.dtype],
+                                      GG_DT[out.dtype], _p(lhs_scale), _p(rhs_scale), _p(status), _stream(dev))
+    _check(code, "ragged_dot_m_noalloc")
     return out
 
 

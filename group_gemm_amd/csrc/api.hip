@@ -5,8 +5,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "groupgemm.h"
 #include "launch.hpp"
+
+// Scratch of ragged_dot_m_noalloc: the per-call state that the workspace holds for the other
+// calls (status word at offset 0, the 8 tile-queue counters at offset 64), kept in a
+// file-scope device array for callers that cannot allocate.  Each GPU holds its own copy
+// for the life of the process; every no-allocation call on a GPU shares it.
+constexpr size_t kScratchBytes = 256;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -147,6 +156,23 @@ gg_status run_k(const void* lhs, const void* dout, const int32_t* gs, void* out,
     return e == hipSuccess ? GG_OK : GG_ERR_HIP;
 }
 
+// Device address of `scratch` on the current device, resolved once per device with that
+// device current (host code must never pass the array's own name: that is a host-side
+// stand-in, not a device address).  NULL if the lookup fails.
+void* scratch_address() {
+    static std::mutex mu;
+    static void* addr[64] = {nullptr};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
 bool m_dtypes_ok(gg_dtype in, gg_dtype out) {
     if (in == GG_DT_F32) return out == GG_DT_F32;
     if (in == GG_DT_BF16 || in == GG_DT_E4M3) return out == GG_DT_BF16 || out == GG_DT_F32;
@@ -223,6 +249,30 @@ gg_status ragged_dot_m(const void* lhs, const void* rhs, const int32_t* group_si
     }
     return run_m(lhs, rhs, group_sizes, out, m, k, n, g, in_dtype, out_dtype, lhs_scale, rhs_scale, (uint32_t*)workspace, workspace,
                  0, (hipStream_t)stream);
+}
+
+gg_status ragged_dot_m_noalloc(const void* lhs, const void* rhs, const int32_t* group_sizes, void* out, int64_t m,
+                               int64_t k, int64_t n, int32_t g, gg_dtype in_dtype, gg_dtype out_dtype,
+                               const uint8_t* lhs_scale, const uint8_t* rhs_scale, uint32_t* status, void* stream) {
+    // the scratch must hold what the workspace of ragged_dot_m would (the same for any shape)
+    const size_t need = gg_workspace_bytes(GG_OP_RAGGED_M, m, k, n, g, 0, in_dtype);
+    if (need > kScratchBytes) return GG_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(status, 4)) return GG_ERR_MISALIGNED;
+    void* ws = scratch_address();
+    if (!ws) return GG_ERR_HIP;
+    gg_status st = check_common(m, k, n, g, group_sizes, ws, kScratchBytes, kHeader);
+    if (st != GG_OK) return st;
+    if (!m_dtypes_ok(in_dtype, out_dtype)) return GG_ERR_BAD_DTYPE;
+    if ((m * k > 0 && !lhs) || (k * n > 0 && !rhs) || (m * n > 0 && !out)) return GG_ERR_NULL_PTR;
+    const size_t es = elem_bytes(in_dtype);
+    if (!aligned(lhs, es) || !aligned(rhs, es) || !aligned(out, elem_bytes(out_dtype))) return GG_ERR_MISALIGNED;
+    if (in_dtype == GG_DT_E4M3) {
+        if (k % 32 != 0) return GG_ERR_UNSUPPORTED;
+        if ((m * k > 0 && !lhs_scale) || (k * n > 0 && !rhs_scale)) return GG_ERR_NULL_PTR;
+        if (!aligned(lhs, 16) || !aligned(rhs, 16)) return GG_ERR_MISALIGNED;
+    }
+    return run_m(lhs, rhs, group_sizes, out, m, k, n, g, in_dtype, out_dtype, lhs_scale, rhs_scale,
+                 status ? status : (uint32_t*)ws, ws, 0, (hipStream_t)stream);
 }
 
 gg_status ragged_dot_m_nk(const void* lhs, const void* rhs_nk, const int32_t* group_sizes, void* out, int64_t m,

@@ -105,6 +105,24 @@ gg_status ragged_dot_m(const void* lhs, const void* rhs, const int32_t* group_si
                        gg_dtype out_dtype, const uint8_t* lhs_scale, const uint8_t* rhs_scale,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* ragged_dot_m_noalloc -- ragged_dot_m for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument.  The per-call state that ragged_dot_m keeps in its workspace (256
+ * bytes: the status word and the forward kernels' tile-queue counters) lives in a static
+ * 256-byte device array of the library instead, one per GPU, held until the process ends;
+ * the call allocates nothing, and a size whose state would not fit returns
+ * GG_ERR_WORKSPACE_TOO_SMALL (no shape does at present).
+ *   status: optional device uint32 that receives the GG_DEV_* bits of this call (NULL: they
+ *     stay in the library's array, where no call reads them).
+ * Other arguments, results and errors as ragged_dot_m (same kernels, bit-identical output).
+ * Every no-allocation call on one GPU shares that array: calls that overlap in time on one
+ * GPU (different streams, or host threads) race and must not be issued.  The first call on
+ * a device looks up the array's address there (not a stream operation). */
+gg_status ragged_dot_m_noalloc(const void* lhs, const void* rhs, const int32_t* group_sizes, void* out,
+                               int64_t m, int64_t k, int64_t n, int32_t g, gg_dtype in_dtype,
+                               gg_dtype out_dtype, const uint8_t* lhs_scale, const uint8_t* rhs_scale,
+                               uint32_t* status, void* stream);
+
 /* ragged_dot_m_nk -- ragged_dot_m with each group's matrix stored [n, k] (k contiguous):
  * the data-gradient classes, which contract the weight's output-feature axis.
  * ("Group-GEMM in XLA", Part 4 Table 7, classes dgrad_wi and dgrad_wo: rhs contracting
