@@ -174,7 +174,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(KParams p) {
             constexpr int NB = decltype(nb_c)::value;
             constexpr int HALF = decltype(half_c)::value;   // ring loads: 0 none, 1 the first PER / 2, 2 the rest
             constexpr int NM = NB * NJ, NR = NB > 0 ? NB + NJ : 0, ND = HALF ? PER / 2 : 0;
-            constexpr int SP = ND > 0 && NM >= ND ? NM / ND : 1;   // MFMAs between two ring loads
+            constexpr int SP = ND > 0 && NM >= ND ? NM / (ND > 0 ? ND : 1) : 1;   // MFMAs between two ring loads
             constexpr int LD = ND > 0 ? (ND - 1) * SP + 1 : 0;
             constexpr int NOPS = NM > NR ? (NM > LD ? NM : LD) : (NR > LD ? NR : LD);
             static_for<0, NOPS>([&](auto o_c) {

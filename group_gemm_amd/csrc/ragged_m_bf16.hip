@@ -264,7 +264,7 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
             constexpr int NB = decltype(nb_c)::value;
             constexpr int ND = decltype(nd_c)::value;
             constexpr int NM = NB * NJ, NR = NB > 0 ? NB + NJ : 0;
-            constexpr int SP = ND > 0 && NM >= ND ? NM / ND : 1;   // MFMAs between two ring loads
+            constexpr int SP = ND > 0 && NM >= ND ? NM / (ND > 0 ? ND : 1) : 1;   // MFMAs between two ring loads
             constexpr int LD = ND > 0 ? (ND - 1) * SP + 1 : 0;
             constexpr int NOPS = NM > NR ? (NM > LD ? NM : LD) : (NR > LD ? NR : LD);
             static_for<0, NOPS>([&](auto o_c) {
@@ -386,7 +386,7 @@ hipError_t launch_clear_queues(int* q, hipStream_t s) {
 
 template <bool B_NK, bool EPI>
 static void launch_mb(const MParams& p, int grid, hipStream_t s) {
-    if (p.tile_queue) launch_clear_queues(p.tile_queue, s);
+    if (p.tile_queue && launch_clear_queues(p.tile_queue, s) != hipSuccess) return;   // reported by the caller
     constexpr int nt = mb::Cfg<GG_TILE>::NT;
     if (p.out_f32) hipLaunchKernelGGL((mb::kernel<GG_TILE, B_NK, EPI, float>), dim3(grid), dim3(nt), 0, s, p);
     else hipLaunchKernelGGL((mb::kernel<GG_TILE, B_NK, EPI, uint16_t>), dim3(grid), dim3(nt), 0, s, p);

@@ -240,7 +240,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
                 constexpr bool DMA = decltype(dma_c)::value;
                 constexpr int NM = 2 * NB, ND = DMA ? PER - PER / 2 : 0, NR = NB > 0 ? 2 : 0;
                 constexpr int NOPS = ND + NR;
-                constexpr int PERM = NM > 0 ? (NOPS + NM - 1) / NM : NOPS;   // ops after each MFMA
+                constexpr int PERM = NM > 0 ? (NOPS + NM - 1) / (NM > 0 ? NM : 1) : NOPS;   // ops after each MFMA
                 constexpr int NSLOT = NM > 0 ? NM : 1;
                 static_for<0, NSLOT>([&](auto m_c) {
                     constexpr int m = decltype(m_c)::value;

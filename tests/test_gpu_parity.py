@@ -125,6 +125,10 @@ M_CASES = [
     # empty groups, and 1000 rows past the groups' total (zero tiles in the same walk)
     (4000, 128, 2304, [0, 17, 300, 1, 256, 129, 700, 5, 0, 64, 128, 127, 257, 33, 90, 200, 11, 0, 40, 60,
                        3, 8, 100, 2, 0, 50, 12, 7, 1, 399]),
+    # groups of 512+ rows on average with short last m-tiles (44, 10, 96, 97 rows); rows
+    # past the total
+    (1600, 256, 520, [300, 0, 1290]),
+    (2200, 192, 264, [352, 609, 1153]),
 ]
 
 
@@ -283,6 +287,7 @@ NK_CASES = [
     (513, 96, 136, [257, 256]),
     (700, 264, 128, [1, 255, 256, 150, 0, 1]),   # k tail (264 = 8 slices + 8), sum < m
     (1100, 1024, 1000, [0, 600, 7, 300, 193]),
+    (1600, 264, 520, [300, 0, 1290]),   # short last m-tiles, k tail
 ]
 
 
