@@ -129,6 +129,11 @@ M_CASES = [
     # past the total
     (1600, 256, 520, [300, 0, 1290]),
     (2200, 192, 264, [352, 609, 1153]),
+    # few output tiles and a long k (the last with a k tail inside a slice); rows past the
+    # total stay zero
+    (1000, 4096, 520, [300, 0, 600, 50]),
+    (700, 8192, 264, [1, 255, 256, 150, 0, 38]),
+    (600, 5000, 136, [290, 0, 300]),
 ]
 
 
@@ -288,6 +293,7 @@ NK_CASES = [
     (700, 264, 128, [1, 255, 256, 150, 0, 1]),   # k tail (264 = 8 slices + 8), sum < m
     (1100, 1024, 1000, [0, 600, 7, 300, 193]),
     (1600, 264, 520, [300, 0, 1290]),   # short last m-tiles, k tail
+    (600, 6144, 264, [300, 200]),        # long k, few tiles, rows past the total
 ]
 
 
