@@ -273,7 +273,7 @@ def ingest_traffic(a):
         per = {}
         for ctr, pre in (("FETCH_SIZE", "fetch_"), ("WRITE_SIZE", "write_")):
             rows = _pmc_rows(os.path.join(d, pre + wl), ctr)
-            ours = {k: v for k, v in rows.items() if k.startswith("void gg::")}
+            ours = {k: v for k, v in rows.items() if k.startswith("void gg::") or k.startswith("gg::")}
             kern = max(ours, key=lambda k: sum(ours[k]))
             per[ctr] = (kern, sum(ours[kern]) / len(ours[kern]) * 1024.0 * copy[ctr], len(ours[kern]))
         table[wl] = {"kernel": per["FETCH_SIZE"][0], "dispatches": per["FETCH_SIZE"][2],
