@@ -261,6 +261,56 @@ def test_mxfp8_random_scales_and_mutants(m, k, n, gs):
     assert not within(oracle.ragged_dot_m(lhs, rhs, np.array(gs, np.int32), ls, np.full_like(rs, 127)))
 
 
+def test_mxfp8_run_summation():
+    """Products in different 32-element blocks are added exactly (fp32): 1.0 in block 0 plus
+    2^-e in block 1 (its own E8M0 scale) gives 1 + 2^-e for e up to 20, as the oracle does."""
+    say("mxfp8 summation across blocks")
+    k, n = 128, 16
+    E = [4, 8, 12, 13, 14, 16, 18, 20]
+    lhs = np.zeros((1, k), np.uint8)
+    lhs[0, 0] = lhs[0, 32] = 0x38                                # e4m3 1.0 at k = 0 and 32
+    rhs = np.zeros((1, k, n), np.uint8)
+    ls, rs = np.full((1, k // 32), 127, np.uint8), np.full((1, k // 32, n), 127, np.uint8)
+    for c, e in enumerate(E):
+        rhs[0, 0, c] = rhs[0, 32, c] = 0x38
+        rs[0, 1, c] = 127 - e                                    # block 1 of column c scaled by 2^-e
+    ref = oracle.ragged_dot_m(lhs, rhs, np.array([1], np.int32), ls, rs)[0]
+    T = lambda a: torch.from_numpy(a).to(DEV)
+    y = gg().ragged_dot_m(T(lhs), T(rhs), T(np.array([1], np.int32)), out_dtype=torch.float32, lhs_scale=T(ls),
+                          rhs_scale=T(rs))
+    torch.cuda.synchronize()
+    y = y.double().cpu().numpy()[0]
+    for c, e in enumerate(E):
+        assert ref[c] == 1.0 + 2.0 ** -e and y[c] == ref[c], f"1 + 2^-{e} across blocks: got 1 + {y[c] - 1:.3e}"
+    assert np.all(y[len(E):] == 0)
+
+
+def test_mxfp8_run_truncation():
+    """Within one run of eight k the scaled fp8 MFMA drops the bits of a product more than 13
+    places below the run's largest product (1 + 2^-13 kept, 1 + 2^-14 .. 2^-18 give 1.0): the
+    measured behaviour the MXFP8 fp32-output reading rests on."""
+    say("mxfp8 run truncation")
+    k, n = 128, 16
+    lhs = np.zeros((1, k), np.uint8)
+    lhs[0, 0] = 0x38          # 1.0
+    lhs[0, 1] = 0x01          # 2^-9
+    rhs = np.zeros((1, k, n), np.uint8)
+    ls, rs = np.full((1, k // 32), 127, np.uint8), np.full((1, k // 32, n), 127, np.uint8)
+    code = {0: 0x38, 1: 0x30, 2: 0x28, 3: 0x20, 4: 0x18, 5: 0x10, 6: 0x08, 7: 0x04, 8: 0x02, 9: 0x01}   # 2^-j
+    for c in range(10):
+        rhs[0, 0, c] = 0x38
+        rhs[0, 1, c] = code[c]   # product 2^-(9 + c) beside 1.0 in the same run
+    T = lambda a: torch.from_numpy(a).to(DEV)
+    y = gg().ragged_dot_m(T(lhs), T(rhs), T(np.array([1], np.int32)), out_dtype=torch.float32, lhs_scale=T(ls),
+                          rhs_scale=T(rs))
+    torch.cuda.synchronize()
+    y = y.double().cpu().numpy()[0]
+    for c in range(10):
+        e = 9 + c
+        want = 1.0 + 2.0 ** -e if e <= 13 else 1.0
+        assert y[c] == want, f"1 + 2^-{e}: got 1 + {y[c] - 1:.3e}"
+
+
 def test_mxfp8_fp32_out_precision():
     """What the scaled fp8 MFMA's summation costs on MX-quantised N(0,1) operands with an
     fp32 result: the error does not grow with k (it comes from the instruction's truncating
