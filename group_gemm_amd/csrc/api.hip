@@ -55,12 +55,21 @@ int persistent_grid(int64_t tile_bound, int per_cu, int cus) {
 
 bool fits_i32(int64_t x) { return x >= 0 && x <= INT32_MAX; }
 
+// Shape and group-size checks shared by every entry point.
+gg_status check_shape(int64_t m, int64_t k, int64_t n, int32_t g, const int32_t* gs) {
+    if (!gs) return GG_ERR_NULL_PTR;
+    if (m < 0 || k < 0 || n < 0 || g < 1 || g > GG_MAX_GROUPS) return GG_ERR_BAD_SHAPE;
+    if (!fits_i32(m) || !fits_i32(k) || !fits_i32(n)) return GG_ERR_BAD_SHAPE;
+    if (!aligned(gs, 4)) return GG_ERR_MISALIGNED;
+    return GG_OK;
+}
+
 gg_status check_common(int64_t m, int64_t k, int64_t n, int32_t g, const int32_t* gs, void* ws, size_t ws_bytes,
                        size_t need) {
     if (!gs || !ws) return GG_ERR_NULL_PTR;
-    if (m < 0 || k < 0 || n < 0 || g < 1 || g > GG_MAX_GROUPS) return GG_ERR_BAD_SHAPE;
-    if (!fits_i32(m) || !fits_i32(k) || !fits_i32(n)) return GG_ERR_BAD_SHAPE;
-    if (!aligned(ws, 16) || !aligned(gs, 4)) return GG_ERR_MISALIGNED;
+    gg_status st = check_shape(m, k, n, g, gs);
+    if (st != GG_OK) return st;
+    if (!aligned(ws, 16)) return GG_ERR_MISALIGNED;
     if (ws_bytes < need) return GG_ERR_WORKSPACE_TOO_SMALL;
     return GG_OK;
 }
@@ -200,6 +209,7 @@ const char* gg_status_string(gg_status s) {
         case GG_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
         case GG_ERR_UNSUPPORTED: return "unsupported argument combination";
         case GG_ERR_HIP: return "HIP runtime error";
+        default: break;
     }
     return "unknown status";
 }
@@ -229,6 +239,7 @@ size_t gg_workspace_bytes(gg_op op, int64_t m, int64_t k, int64_t n, int32_t g, 
             const gg::PermuteGeometry pg = gg::permute_geometry(m);
             return kHeader + align_up((size_t)pg.nblk * (size_t)g * 4, 256) + align_up((size_t)pg.nblk * 4, 256);
         }
+        default: break;
     }
     return 0;
 }
@@ -258,9 +269,7 @@ gg_status ragged_dot_m_noalloc(const void* lhs, const void* rhs, const int32_t* 
     const size_t need = gg_workspace_bytes(GG_OP_RAGGED_M, m, k, n, g, 0, in_dtype);
     if (need > kScratchBytes) return GG_ERR_WORKSPACE_TOO_SMALL;
     if (!aligned(status, 4)) return GG_ERR_MISALIGNED;
-    void* ws = scratch_address();
-    if (!ws) return GG_ERR_HIP;
-    gg_status st = check_common(m, k, n, g, group_sizes, ws, kScratchBytes, kHeader);
+    gg_status st = check_shape(m, k, n, g, group_sizes);
     if (st != GG_OK) return st;
     if (!m_dtypes_ok(in_dtype, out_dtype)) return GG_ERR_BAD_DTYPE;
     if ((m * k > 0 && !lhs) || (k * n > 0 && !rhs) || (m * n > 0 && !out)) return GG_ERR_NULL_PTR;
@@ -271,6 +280,8 @@ gg_status ragged_dot_m_noalloc(const void* lhs, const void* rhs, const int32_t* 
         if ((m * k > 0 && !lhs_scale) || (k * n > 0 && !rhs_scale)) return GG_ERR_NULL_PTR;
         if (!aligned(lhs, 16) || !aligned(rhs, 16)) return GG_ERR_MISALIGNED;
     }
+    void* ws = scratch_address();   // looked up only once every argument has passed its check
+    if (!ws) return GG_ERR_HIP;
     return run_m(lhs, rhs, group_sizes, out, m, k, n, g, in_dtype, out_dtype, lhs_scale, rhs_scale,
                  status ? status : (uint32_t*)ws, ws, 0, (hipStream_t)stream);
 }

@@ -45,6 +45,10 @@ extern "C" {
 
 #define GG_ABI_VERSION 5
 
+/* Each enumeration below also names the ends of the int32 range, so that every int32 value a
+ * caller passes (from C, through an FFI, ...) is a valid value of the type; the calls refuse the
+ * ones they do not know with an error code. */
+
 typedef enum {
     GG_OK = 0,
     GG_ERR_NULL_PTR = 1,           /* a required pointer is NULL                          */
@@ -53,13 +57,15 @@ typedef enum {
     GG_ERR_MISALIGNED = 4,         /* a pointer is not aligned to its element (16 B for e4m3) */
     GG_ERR_WORKSPACE_TOO_SMALL = 5,
     GG_ERR_UNSUPPORTED = 6,        /* e.g. MXFP8 with k not a multiple of 32               */
-    GG_ERR_HIP = 7                 /* a HIP runtime call failed (launch, device query)      */
+    GG_ERR_HIP = 7,                /* a HIP runtime call failed (launch, device query)      */
+    GG_STATUS_RANGE_MIN = INT32_MIN, GG_STATUS_RANGE_MAX = INT32_MAX
 } gg_status;
 
 typedef enum {
     GG_DT_F32 = 0,                 /* IEEE binary32                                         */
     GG_DT_BF16 = 1,                /* bfloat16                                              */
-    GG_DT_E4M3 = 2                 /* OCP float8 e4m3 ("e4m3fn"), with E8M0 block scales    */
+    GG_DT_E4M3 = 2,                /* OCP float8 e4m3 ("e4m3fn"), with E8M0 block scales    */
+    GG_DT_RANGE_MIN = INT32_MIN, GG_DT_RANGE_MAX = INT32_MAX
 } gg_dtype;
 
 typedef enum {
@@ -67,12 +73,14 @@ typedef enum {
     GG_OP_RAGGED_K = 1,            /* ragged_dot_k                                          */
     GG_OP_PADDED_M = 2,            /* padded_dot, non-contracting form                      */
     GG_OP_PADDED_K = 3,            /* padded_dot, contracting form                          */
-    GG_OP_PERMUTE = 4              /* moe_permute (m = tokens * top_k copies)               */
+    GG_OP_PERMUTE = 4,             /* moe_permute (m = tokens * top_k copies)               */
+    GG_OP_RANGE_MIN = INT32_MIN, GG_OP_RANGE_MAX = INT32_MAX
 } gg_op;
 
 typedef enum {
     GG_ACT_SILU = 0,               /* x * sigmoid(x)  (SwiGLU when applied to the gate)     */
-    GG_ACT_GELU_TANH = 1           /* 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))       */
+    GG_ACT_GELU_TANH = 1,          /* 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))       */
+    GG_ACT_RANGE_MIN = INT32_MIN, GG_ACT_RANGE_MAX = INT32_MAX
 } gg_activation;
 
 /* Device status bits (read back with gg_read_device_status). */
