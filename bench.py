@@ -56,6 +56,9 @@ def parse():
                          "write_<workload>, copy_fetch, copy_write) and record the HBM bytes per launch "
                          "of each workload's dominant kernel in profiles/traffic.json")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30, help="byte count the copy probe was run with")
+    ap.add_argument("--library-context", action="store_true",
+                    help="only time torch's own GEMMs (hipBLASLt) on the same inputs, for context: the "
+                         "bf16 workloads as one matmul per group and as one dense matmul of the same flops")
     return ap.parse_args()
 
 
@@ -394,6 +397,39 @@ def run_workload(name, a, torch, G, W, dev, cpu=True):
     return rec
 
 
+def library_context(a, torch, W, dev):
+    """torch.matmul (hipBLASLt on ROCm) on the bf16 workloads' own inputs: one call per
+    non-empty group (the loop a framework without a grouped kernel runs) and one dense call of
+    the same flops.  Context for the roofline fractions only; nothing here is the library."""
+    res = {}
+    for name in ("mixtral8x7b_up_bf16", "deepseekv3_routed_bf16", "llama4scout_wgrad_bf16"):
+        w = W.WORKLOADS[name]
+        gs = W.group_sizes(w)
+        d = W.make_inputs(w, device=dev, gs=gs)
+        offs = np.concatenate([[0], np.cumsum(gs)]).astype(np.int64)
+        live = [h for h in range(w.g) if gs[h] > 0]
+        flops = useful_flops(w, gs)
+        lhs = d["lhs"]
+        if w.op == "k":
+            dout = d["dout"]
+            per_group = lambda: [torch.matmul(lhs[offs[h]:offs[h + 1]].t(), dout[offs[h]:offs[h + 1]]) for h in live]
+            rows = int(gs.sum())
+            dense = lambda: torch.matmul(lhs[:rows].t(), dout[:rows])
+        else:
+            rhs = d["rhs"]
+            per_group = lambda: [torch.matmul(lhs[offs[h]:offs[h + 1]], rhs[h]) for h in live]
+            wide = torch.empty((w.k, w.n), dtype=torch.bfloat16, device=dev).copy_(rhs[0])
+            dense = lambda: torch.matmul(lhs[:int(gs.sum())], wide)
+        entry = {}
+        for kind, fn in (("per_group", per_group), ("dense_same_flops", dense)):
+            _, per = time_calls(fn, a.steps, a.warmup, torch)
+            med = float(np.median(per))
+            entry[kind] = {"median_us": round(med * 1e6, 1), "tflops": round(flops / med / 1e12, 1)}
+        res[name] = entry
+        del d
+    print(json.dumps({"library_context": "torch.matmul (hipBLASLt), bf16 in / bf16 out", "workloads": res}), flush=True)
+
+
 def main():
     a = parse()
     if a.traffic_from:
@@ -415,6 +451,10 @@ def main():
     import group_gemm_amd as G
     from group_gemm_amd import workloads as W
 
+    if a.library_context:
+        torch.cuda.set_device(0)
+        library_context(a, torch, W, "cuda:0")
+        return
     G.lib()   # fail loudly if the HIP library is missing
     dev = "cuda:0"
     torch.cuda.set_device(0)
