@@ -13,9 +13,10 @@
 // LDS ring of 32-row slices filled by direct-to-LDS loads, two pinned half-slice phases.
 // Both operands have the contracted rows as their slow axis, so both slices are
 // [32 rows][256 columns] in the layout of the non-contracting kernel's weight slice, and
-// both are read with ds_read_b64_tr_b16 into row-consecutive fragments.  The buffer
-// descriptors cover only the group's rows, so the last slice's rows past the group read
-// as zeros.  An empty group still owns its tiles: they store exact zeros.
+// both are read with ds_read_b64_tr_b16 into row-consecutive fragments.  The ring loads'
+// buffer descriptors cover only the group's rows (one 32-row slice at a time when lhs or dout
+// spans 2 GiB or more, so a group of any size stays within 32-bit offsets), and the last
+// slice's rows past the group read as zeros.  An empty group still owns its tiles: they store exact zeros.
 // Order: groups longest first (even rounds for the persistent walk), and within a group
 // 4 x 8 (k-tile, n-tile) super-tiles, so the 32 tiles running on one XCD share operand
 // slices in L2.
@@ -71,7 +72,7 @@ __device__ inline void read_one(Frags& f, const uint16_t* a, const uint16_t* b, 
     else f.b[R == 0 ? 0 : R - NB] = frag(b, s, c0w, R == 0 ? 0 : R - NB);
 }
 
-template <bool EPI, typename OutT>
+template <bool EPI, typename OutT, bool REBASE>
 __global__ __launch_bounds__(NT, 1) void kernel(KParams p) {
     __shared__ Smem sm;
     const int t = threadIdx.x, l = t & 63, wave = t >> 6;
@@ -140,22 +141,40 @@ __global__ __launch_bounds__(NT, 1) void kernel(KParams p) {
         const int nb = max(0, min(MI, cdiv(rows_valid - r0w, 32)));
         const int nk = cdiv(size, BR);
 
-        const i32x4 ra = make_rsrc_v((const uint16_t*)p.lhs + (size_t)row_base * p.k, (uint32_t)size * k2);
-        const i32x4 rb = make_rsrc_v((const uint16_t*)p.dout + (size_t)row_base * p.n, (uint32_t)size * n2);
-        // ring load d (lhs blocks 0-3, dout blocks 4-7) of row slice `stage`; slices past the
-        // group are zero-filled into the slot no one reads
-        auto dma_one = [&](auto d_c, int stage) {
+        // ring load d (lhs blocks 0-3, dout blocks 4-7) of row slice `stage`.  Each load's buffer
+        // descriptor starts at the slice's first row and covers only its rows of the group, so
+        // the 32-bit offsets span one slice whatever the group's size, and rows past the group
+        // (and slices past its end) read as zeros into the slot no one reads.
+        // Buffer descriptors of the ring loads: with REBASE each covers one 32-row slice (its
+        // rows of the group), so a group of any size stays within 32-bit offsets; otherwise one
+        // pair covers the group's rows (every row of lhs / dout spans less than 2 GiB).  Either
+        // way rows past the group, and slices past its end, read as zeros into a slot no one reads.
+        struct SliceRsrc { i32x4 a, b; };
+        const SliceRsrc group_rs = REBASE ? SliceRsrc{} : SliceRsrc{
+            make_rsrc_v((const uint16_t*)p.lhs + (size_t)row_base * p.k, (uint32_t)size * k2),
+            make_rsrc_v((const uint16_t*)p.dout + (size_t)row_base * p.n, (uint32_t)size * n2)};
+        auto slice_rsrc = [&](int stage) {
+            if constexpr (!REBASE) return group_rs;
+            const bool live = stage < nk;
+            const int srows = live ? min(BR, size - stage * BR) : 0;
+            const size_t row0 = (size_t)row_base + (size_t)(live ? stage * BR : 0);
+            return SliceRsrc{make_rsrc_v((const uint16_t*)p.lhs + row0 * p.k, (uint32_t)srows * k2),
+                             make_rsrc_v((const uint16_t*)p.dout + row0 * p.n, (uint32_t)srows * n2)};
+        };
+        // ring load d (lhs blocks 0-3, dout blocks 4-7) of row slice `stage`
+        auto dma_one = [&](auto d_c, int stage, const SliceRsrc& r) {
             constexpr int d = decltype(d_c)::value;
             constexpr int u = d & 3;
             const int slot = stage % STAGES;
             const bool live = stage < nk;
-            const uint32_t rpart = (uint32_t)(stage * BR + 2 * (4 * wave_u + u));
+            // row within the descriptor
+            const uint32_t rrow = (uint32_t)((REBASE ? 0 : stage * BR) + 2 * (4 * wave_u + u));
             if constexpr (d < 4) {
                 const bool ok = live && ch8[u] < p.k - i0;
-                load_lds16(ra, lds_a + (uint32_t)slot * (SLICE * 2) + u * 1024u, ok ? a_lane[u] + rpart * k2 + (uint32_t)i0 * 2u : kOOB);
+                load_lds16(r.a, lds_a + (uint32_t)slot * (SLICE * 2) + u * 1024u, ok ? a_lane[u] + rrow * k2 + (uint32_t)i0 * 2u : kOOB);
             } else {
                 const bool ok = live && ch8[u] < p.n - j0;
-                load_lds16(rb, lds_b + (uint32_t)slot * (SLICE * 2) + u * 1024u, ok ? b_lane[u] + rpart * n2 + (uint32_t)j0 * 2u : kOOB);
+                load_lds16(r.b, lds_b + (uint32_t)slot * (SLICE * 2) + u * 1024u, ok ? b_lane[u] + rrow * n2 + (uint32_t)j0 * 2u : kOOB);
             }
         };
 
@@ -177,6 +196,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(KParams p) {
             constexpr int SP = ND > 0 && NM >= ND ? NM / (ND > 0 ? ND : 1) : 1;   // MFMAs between two ring loads
             constexpr int LD = ND > 0 ? (ND - 1) * SP + 1 : 0;
             constexpr int NOPS = NM > NR ? (NM > LD ? NM : LD) : (NR > LD ? NR : LD);
+            const SliceRsrc rs = slice_rsrc(stage);
             static_for<0, NOPS>([&](auto o_c) {
                 constexpr int o = decltype(o_c)::value;
                 if constexpr (o < NM) {
@@ -184,7 +204,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(KParams p) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
                 }
                 if constexpr (ND > 0 && o % SP == 0 && o / SP < ND)
-                    dma_one(std::integral_constant<int, (HALF - 1) * (PER / 2) + o / SP>{}, stage);
+                    dma_one(std::integral_constant<int, (HALF - 1) * (PER / 2) + o / SP>{}, stage, rs);
                 if constexpr (o < NR) read_one<NB, o>(nxt, a, b, s, r0w, c0w);
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -197,8 +217,12 @@ __global__ __launch_bounds__(NT, 1) void kernel(KParams p) {
             // half slice of iteration s - 4 (its slot is free once that iteration's barrier has
             // passed), the rest in the first half slice of iteration s - 3; either way
             // PER * (STAGES - 2) loads follow slice kt + 1's last one when iteration kt waits
-            static_for<0, STAGES - 1>([&](auto st_c) { static_for<0, PER>([&](auto d_c) { dma_one(d_c, decltype(st_c)::value); }); });
-            static_for<0, PER / 2>([&](auto d_c) { dma_one(d_c, STAGES - 1); });
+            static_for<0, STAGES - 1>([&](auto st_c) {
+                const SliceRsrc rs = slice_rsrc(decltype(st_c)::value);
+                static_for<0, PER>([&](auto d_c) { dma_one(d_c, decltype(st_c)::value, rs); });
+            });
+            const SliceRsrc rs3 = slice_rsrc(STAGES - 1);
+            static_for<0, PER / 2>([&](auto d_c) { dma_one(d_c, STAGES - 1, rs3); });
             wait_vm<PER * (STAGES - 2) + PER / 2>();   // slice 0 in LDS
             lds_barrier();
             if constexpr (NB > 0) static_for<0, NB + NJ>([&](auto r_c) { read_one<NB, decltype(r_c)::value>(f0, sm.ring.a[0], sm.ring.b[0], 0, r0w, c0w); });
@@ -236,22 +260,31 @@ __global__ __launch_bounds__(NT, 1) void kernel(KParams p) {
 }  // namespace kr
 
 bool ragged_k_bf16_fast_ok(const KParams& p) {
-    // 32-bit buffer offsets over the whole lhs / dout (a group may own every row) and over
-    // one 256-row tile of the output
-    const uint64_t a = (uint64_t)p.m * (uint64_t)p.k * 2u + 64ull * p.k * 2u;
-    const uint64_t b = (uint64_t)p.m * (uint64_t)p.n * 2u + 64ull * p.n * 2u;
+    // 32-bit buffer offsets over one 32-row slice of lhs / dout and one 256-row output tile
+    const uint64_t a = 33ull * (uint64_t)p.k * 2u;
+    const uint64_t b = 33ull * (uint64_t)p.n * 2u;
     const uint64_t o = 256ull * (uint64_t)p.n * 4u;
     return p.k % 8 == 0 && p.n % 8 == 0 && a < (1ull << 31) && b < (1ull << 31) && o < (1ull << 31);
 }
 
-hipError_t launch_ragged_k_bf16_fast(const KParams& p, int grid, hipStream_t s) {
+template <bool REBASE>
+static void launch_kr(const KParams& p, int grid, hipStream_t s) {
     if (p.epi) {
-        if (p.out_f32) hipLaunchKernelGGL((kr::kernel<true, float>), dim3(grid), dim3(kr::NT), 0, s, p);
-        else hipLaunchKernelGGL((kr::kernel<true, uint16_t>), dim3(grid), dim3(kr::NT), 0, s, p);
+        if (p.out_f32) hipLaunchKernelGGL((kr::kernel<true, float, REBASE>), dim3(grid), dim3(kr::NT), 0, s, p);
+        else hipLaunchKernelGGL((kr::kernel<true, uint16_t, REBASE>), dim3(grid), dim3(kr::NT), 0, s, p);
     } else {
-        if (p.out_f32) hipLaunchKernelGGL((kr::kernel<false, float>), dim3(grid), dim3(kr::NT), 0, s, p);
-        else hipLaunchKernelGGL((kr::kernel<false, uint16_t>), dim3(grid), dim3(kr::NT), 0, s, p);
+        if (p.out_f32) hipLaunchKernelGGL((kr::kernel<false, float, REBASE>), dim3(grid), dim3(kr::NT), 0, s, p);
+        else hipLaunchKernelGGL((kr::kernel<false, uint16_t, REBASE>), dim3(grid), dim3(kr::NT), 0, s, p);
     }
+}
+
+hipError_t launch_ragged_k_bf16_fast(const KParams& p, int grid, hipStream_t s) {
+    // one descriptor per group while all of lhs and dout (a group may own every row) spans
+    // less than 2 GiB; per-slice descriptors beyond that
+    const uint64_t a = (uint64_t)p.m * (uint64_t)p.k * 2u + 64ull * p.k * 2u;
+    const uint64_t b = (uint64_t)p.m * (uint64_t)p.n * 2u + 64ull * p.n * 2u;
+    if (a < (1ull << 31) && b < (1ull << 31)) launch_kr<false>(p, grid, s);
+    else launch_kr<true>(p, grid, s);
     return hipGetLastError();
 }
 

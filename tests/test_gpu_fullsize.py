@@ -129,6 +129,29 @@ def test_full_size_ragged_k():
         assert bool((out[h] == 0).all())
 
 
+def test_ragged_k_group_over_2gib():
+    """A group whose dout rows span more than 2 GiB: the ring loads address one 32-row slice at
+    a time, so the vectorised kernel covers it (k = 64, n = 16384, 68000 rows in one group)."""
+    import group_gemm_amd as G
+    m, k, n = 70000, 64, 16384
+    gs = np.array([68000, 0, 2000], dtype=np.int32)
+    assert m * n * 2 > 2 ** 31
+    say("ragged_dot_k, dout over 2 GiB", m, k, n, gs.tolist())
+    gen = torch.Generator(device=DEV).manual_seed(11)
+    lhs = torch.randn((m, k), generator=gen, device=DEV).to(torch.bfloat16)
+    dout = torch.randn((m, n), generator=gen, device=DEV).to(torch.bfloat16)
+    out = torch.full((3, k, n), float("nan"), dtype=torch.float32, device=DEV)
+    G.ragged_dot_k(lhs, dout, torch.from_numpy(gs).to(DEV), out=out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()), "non-finite output"
+    assert bool((out[1] == 0).all())
+    pairs = np.array([(0, 0), (0, 37), (0, k - 1), (2, 0), (2, 21), (2, k - 1)], dtype=np.int64)
+    ref = oracle.ragged_dot_k(raw(lhs), raw(dout), gs, pairs=pairs)
+    y = out[torch.from_numpy(pairs[:, 0]).to(DEV), torch.from_numpy(pairs[:, 1]).to(DEV)].double().cpu().numpy()
+    rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    assert rel <= 1e-5, f"normwise relative error {rel:.3e} over the sampled rows"
+
+
 def test_full_size_padded_matches_ragged():
     """The padded baseline, at the size the benchmark times it, gives the ragged result."""
     import group_gemm_amd as G
