@@ -392,12 +392,8 @@ __device__ inline void load_tiles(Regs& R, const uint8_t* __restrict__ lhs, cons
         const int r = (t >> 3) + 64 * i;
         const int kc = kk + ((t & 7) << 4);
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < rows_valid && kc < k) {
-            const uint8_t* src = lhs + (size_t)(row0 + r) * (size_t)k + kc;
-            if ((k & 15) == 0) v = *(const uint4*)src;
-            else {   // k % 32 == 0 always holds, so 16-byte chunks never cross k
-                v = *(const uint4*)src;
-            }
+        if (r < rows_valid && kc < k) {   // k % 32 == 0 holds, so a 16-byte chunk never crosses k
+            v = *(const uint4*)(lhs + (size_t)(row0 + r) * (size_t)k + kc);
         }
         R.a[i] = v;
     }
