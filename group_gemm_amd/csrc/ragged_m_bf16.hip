@@ -211,6 +211,11 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
         row0 += mt * BM;
         const int rows_valid = min(BM, size - mt * BM);
         const int col0 = nt * BN;
+        // A group with one m-tile reads each weight slice once (no other tile of it shares the
+        // slice), so its weight loads carry the nontemporal hint: they stream past L2 instead of
+        // evicting the rows that the group's other n-tiles read again (DeepSeek-like workload:
+        // 0.27 GB less fetched per call, 1.2-1.6 % faster; the others have no such group).
+        const bool b_stream = __builtin_amdgcn_readfirstlane(mtg == 1 ? 1 : 0) != 0;
         // 32-row blocks of this wave that hold any of the tile's rows
         const int nb = max(0, min(MI, cdiv(rows_valid - r0w, 32)));
 
@@ -227,9 +232,14 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
             const uint32_t wpart = (uint32_t)(8 * (C::A_LOADS * wave_u + e)) * k2 + (uint32_t)kk * 2u;
             load_lds16(ra, lds_a + (uint32_t)(pr % STAGES) * (C::APAIR * 2) + e * 1024u, ok ? ap_lane[e & 1] + wpart : kOOB);
         };
-        // B block u of k slice st
-        auto dma_b = [&](auto u_c, int st) {
+        // B block u of k slice st (NT: with the nontemporal hint)
+        auto dma_b = [&](auto u_c, int st, auto nt_c) {
             constexpr int u = decltype(u_c)::value;
+            constexpr bool NT_HINT = decltype(nt_c)::value;
+            auto load = [&](uint32_t dst, uint32_t off) {
+                if constexpr (NT_HINT) load_lds16_nt(rb, dst, off);
+                else load_lds16(rb, dst, off);
+            };
             const int kk = st * BK;
             const uint32_t dst = lds_b + (uint32_t)(st % STAGES) * (BSLICE * 2) + u * 1024u;
             if constexpr (B_NK) {
@@ -237,12 +247,12 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
                 // fall outside the descriptor
                 const bool ok = kk + 8 * nk_chunk < p.k;
                 const uint32_t wpart = (uint32_t)(col0 + 16 * (C::B_LOADS * wave_u + u)) * k2 + (uint32_t)kk * 2u;
-                load_lds16(rb, dst, ok ? nk_lane + wpart : kOOB);
+                load(dst, ok ? nk_lane + wpart : kOOB);
             } else {
                 // k row kk + 2 (4 wave + u) + l / 32, columns col0 + b_ch8 .. + 7
                 const bool ok = kk < p.k && b_ch8[u] < p.n - col0;
                 const uint32_t wpart = (uint32_t)(kk + 2 * (C::B_LOADS * wave_u + u)) * n2 + (uint32_t)col0 * 2u;
-                load_lds16(rb, dst, ok ? b_lane[u] + wpart : kOOB);
+                load(dst, ok ? b_lane[u] + wpart : kOOB);
             }
         };
 
@@ -292,7 +302,7 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
         // stores of the previous tile still in flight only raise the count.
         constexpr int AH = C::A_HALF, BL = C::B_LOADS;
         constexpr int W_STEADY = 2 * AH + BL;   // B of slice kt + 1 is followed by A, B, A
-        auto run = [&](auto nb_c) {
+        auto run = [&](auto nb_c, auto nt_c) {
             constexpr int NB = decltype(nb_c)::value;
             constexpr std::integral_constant<int, 0> zero{};
             constexpr std::integral_constant<int, AH> nd_a{};
@@ -300,11 +310,11 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
             Frags<MI, NJ> f0, f1;
             // what iterations before the first would have issued, in an order that leaves at
             // least W_STEADY loads behind slice 1's B blocks before the first barrier
-            static_for<0, BL>([&](auto u_c) { dma_b(u_c, 0); });
+            static_for<0, BL>([&](auto u_c) { dma_b(u_c, 0, nt_c); });
             static_for<0, 2 * AH>([&](auto e_c) { dma_a(e_c, 0); });
-            static_for<0, BL>([&](auto u_c) { dma_b(u_c, 1); });
+            static_for<0, BL>([&](auto u_c) { dma_b(u_c, 1, nt_c); });
             static_for<0, 2 * AH>([&](auto e_c) { dma_a(e_c, 1); });
-            static_for<0, BL>([&](auto u_c) { dma_b(u_c, 2); });
+            static_for<0, BL>([&](auto u_c) { dma_b(u_c, 2, nt_c); });
             wait_vm<2 * BL + 2 * AH>();   // slice 0's B blocks and pair 0 in LDS
             lds_barrier();
             if constexpr (NB > 0)
@@ -320,7 +330,7 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
                       f0, f1, sm.ring.a[pa], 4 * P + 2, sm.ring.b[slot], 1);
                 wait_vm<W_STEADY>();   // slice kt + 1 in LDS
                 lds_barrier();
-                phase(nb_c, nd_b, [&](auto d_c) { dma_b(d_c, kt + 3); }, f1, f0, sm.ring.a[pn], 4 * (1 - P), sm.ring.b[ns], 0);
+                phase(nb_c, nd_b, [&](auto d_c) { dma_b(d_c, kt + 3, nt_c); }, f1, f0, sm.ring.a[pn], 4 * (1 - P), sm.ring.b[ns], 0);
             };
             constexpr std::integral_constant<int, 0> even{};
             constexpr std::integral_constant<int, 1> odd{};
@@ -336,7 +346,12 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
             phase(nb_c, zero, [&](auto) {}, f0, f1, al, 4 * (last & 1) + 2, bl, 1);
             mma<MI, NJ, NB>(f1, acc);
         };
-        if (nk > 0) with_nb<MI>(nb, run);
+        // the hint is a compile-time choice: a branch around each load inside the pinned
+        // schedule measured 8 % slower
+        if (nk > 0) {
+            if (b_stream) with_nb<MI>(nb, [&](auto nb_c) { run(nb_c, std::true_type{}); });
+            else with_nb<MI>(nb, [&](auto nb_c) { run(nb_c, std::false_type{}); });
+        }
         // Every ring load has landed (the zero-fill loads of slices past the end may still be
         // in flight, and the epilogue strips overlap their slots) and every wave is done
         // reading the ring before it is reused.

@@ -47,6 +47,12 @@ __device__ inline void load_lds16(i32x4 r, uint32_t lds_addr, uint32_t off) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :: "s"(lds_addr), "v"(off), "s"(r) : "memory", "m0");
 }
+// the same with the nontemporal hint: for data read once, streamed past the caches so it
+// does not evict operands that other tiles will read again
+__device__ inline void load_lds16_nt(i32x4 r, uint32_t lds_addr, uint32_t off) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :: "s"(lds_addr), "v"(off), "s"(r) : "memory", "m0");
+}
 __device__ inline void load_lds4(i32x4 r, uint32_t lds_addr, uint32_t off) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                  :: "s"(lds_addr), "v"(off), "s"(r) : "memory", "m0");
