@@ -130,9 +130,9 @@ struct EpiTile {
 // (the MFMA took the column operand first).  `ro` covers the tile's valid rows of the
 // output; col0 is the tile's first column.  With STRIP (always for bf16 results and for an
 // epilogue) results go through `strip`, a wave-private 32 x (WCOLS + 4) fp32 area of LDS:
-// the accumulators are written there straight from AGPRs, come back 8 consecutive columns
-// per lane, are converted or scaled (EPI), and leave as 16-byte stores, a whole row segment
-// per WCOLS / 8 lanes.  Converting or scaling in registers would copy every accumulator
+// the accumulators are written there straight from AGPRs, come back 8 columns per lane
+// (8 consecutive ones for bf16, two runs of 4 for fp32), are converted or scaled (EPI), and
+// leave as 16-byte stores, a whole row segment per WCOLS / 8 lanes.  Converting or scaling in registers would copy every accumulator
 // through VGPRs.  Without STRIP, fp32 results are stored straight from AGPRs, a quarter
 // cache line per row and instruction: fewer registers, but slower writes (the fp32
 // weight-gradient kernel, whose output dominates its traffic, takes the strip: 12 % faster).
@@ -161,8 +161,14 @@ __device__ inline void store_acc(const f32x16 (&acc)[MI][NJ], float* strip, rsrc
     }
     constexpr int SP = WCOLS + 4, LPR = WCOLS / 8, RPS = 64 / LPR;
     const int rr = l / LPR, g = l % LPR;
-    const int col = col0 + c0w + 8 * g;
-    const bool col_ok = col < n;
+    // Columns of x[0..3] and x[4..7]: eight consecutive ones for bf16 (one 16-byte store), two
+    // runs of four for fp32, 4 g and WCOLS / 2 + 4 g, so that each 16-byte store instruction
+    // writes whole 128-byte lines (16 lanes cover 64 consecutive columns of a row) instead of
+    // every other 16 bytes of twice as many lines.  n % 8 == 0, so a run is in or out whole.
+    constexpr int HALF = WCOLS / 2;
+    const int sA = osz2 ? 8 * g : 4 * g, sB = osz2 ? 8 * g + 4 : HALF + 4 * g;   // strip columns
+    const int colA = col0 + c0w + sA, colB = col0 + c0w + sB;
+    const bool okA = colA < n, okB = colB < n;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -175,26 +181,27 @@ __device__ inline void store_acc(const f32x16 (&acc)[MI][NJ], float* strip, rsrc
 #pragma unroll
         for (int t2 = 0; t2 < 32 / RPS; ++t2) {
             const int rs = t2 * RPS + rr;   // row within the strip
-            const f32x4 lo = *(const f32x4*)(strip + rs * SP + 8 * g);
-            const f32x4 hi = *(const f32x4*)(strip + rs * SP + 8 * g + 4);
+            const f32x4 lo = *(const f32x4*)(strip + rs * SP + sA);
+            const f32x4 hi = *(const f32x4*)(strip + rs * SP + sB);
             float x[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             const int r = r0w + 32 * i + rs;
-            const uint32_t off = col_ok ? (uint32_t)(r * n + col) * (uint32_t)sizeof(OutT) : kOOB;
+            const uint32_t offA = okA ? (uint32_t)(r * n + colA) * (uint32_t)sizeof(OutT) : kOOB;
+            const uint32_t offB = okB ? (uint32_t)(r * n + colB) * (uint32_t)sizeof(OutT) : kOOB;
             if constexpr (EPI) {
                 float old[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) old[e] = 0.f;
                 if (ep.beta != 0.f) {   // rows past the tile and columns past n read as 0
                     if constexpr (osz2) {
-                        const i32x4 c = __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0);
+                        const i32x4 c = __builtin_amdgcn_raw_buffer_load_b128(ro, offA, 0, 0);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             old[2 * e] = __uint_as_float((uint32_t)c[e] << 16);
                             old[2 * e + 1] = __uint_as_float((uint32_t)c[e] & 0xffff0000u);
                         }
                     } else {
-                        const i32x4 c0 = __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0);
-                        const i32x4 c1 = __builtin_amdgcn_raw_buffer_load_b128(ro, col_ok ? off + 16u : kOOB, 0, 0);
+                        const i32x4 c0 = __builtin_amdgcn_raw_buffer_load_b128(ro, offA, 0, 0);
+                        const i32x4 c1 = __builtin_amdgcn_raw_buffer_load_b128(ro, offB, 0, 0);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             old[e] = __int_as_float(c0[e]);
@@ -205,17 +212,20 @@ __device__ inline void store_acc(const f32x16 (&acc)[MI][NJ], float* strip, rsrc
                 // the bias row is re-read per output row (cached) to keep few registers live
                 float bias[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) bias[e] = ep.bias_row && col + e < n ? ep.bias_row[col + e] : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    bias[e] = ep.bias_row && okA ? ep.bias_row[colA + e] : 0.f;
+                    bias[4 + e] = ep.bias_row && okB ? ep.bias_row[colB + e] : 0.f;
+                }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = ep.alpha * x[e] + bias[e] + ep.beta * old[e];
             }
             if constexpr (osz2) {
                 const i32x4 v = {(int)pack_bf16(x[0], x[1]), (int)pack_bf16(x[2], x[3]), (int)pack_bf16(x[4], x[5]),
                                  (int)pack_bf16(x[6], x[7])};
-                bstore(ro, off, v);
+                bstore(ro, offA, v);
             } else {
-                bstore(ro, off, i32x4{__float_as_int(x[0]), __float_as_int(x[1]), __float_as_int(x[2]), __float_as_int(x[3])});
-                bstore(ro, col_ok ? off + 16u : kOOB, i32x4{__float_as_int(x[4]), __float_as_int(x[5]), __float_as_int(x[6]), __float_as_int(x[7])});
+                bstore(ro, offA, i32x4{__float_as_int(x[0]), __float_as_int(x[1]), __float_as_int(x[2]), __float_as_int(x[3])});
+                bstore(ro, offB, i32x4{__float_as_int(x[4]), __float_as_int(x[5]), __float_as_int(x[6]), __float_as_int(x[7])});
             }
         }
     }
