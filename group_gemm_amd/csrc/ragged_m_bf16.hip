@@ -16,7 +16,8 @@
 //    MFMAs; A (rows) two k slices per slot, so that every load moves 128 contiguous bytes
 //    of a row, landing two iterations before use.  The buffer descriptors bound the
 //    group's rows and the weight matrix, so rows past the group and the k / n tails
-//    arrive as zeros without branches.
+//    arrive as zeros without branches.  A group with a single m-tile streams its weights
+//    with the nontemporal hint (nothing else reads them).
 //  * A rows (k-contiguous) feed the MFMA through ds_read_b128; B rows are n-contiguous
 //    (rhs as given, no per-call relayout) and ds_read_b64_tr_b16 turns them into
 //    k-consecutive fragments.
