@@ -234,6 +234,10 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
                 read_b(f, 0, sm.ring[0], c0w, cp);
                 read_b(f, 1, sm.ring[0], c0w, cp);
             }
+            // Nothing of the prologue's reads stays pending into the loop: the compiler's wait
+            // counts at the loop head merge both ways in, and the prologue's order (reads
+            // just issued) would otherwise make every iteration wait for all reads in flight.
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
             // phase 1 of slice kt: MFMAs (i, 0..1), the second half of the ring loads of slice
             // `stage` (when DMA), reads of B blocks 2, 3 of slot kt
             auto phase1 = [&](auto dma_c, const Slot& s, int stage) {
