@@ -38,7 +38,7 @@ constexpr int BS_BYTES = 2 * 2 * BN;    // 2 copies x the slice's 2 k-block rows
 constexpr int PER = 4 + 4 + 1 + 1;      // ring loads per thread per slice: A, B, A scales, B scales
 static_assert(PER * (STAGES - 1) <= 63, "vmcnt range");
 
-struct Slot {
+struct alignas(16) Slot {
     uint8_t a[A_BYTES];
     uint8_t b[B_BYTES];
     uint8_t as[AS_BYTES];
