@@ -226,6 +226,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(KParams p) {
             wait_vm<PER * (STAGES - 2) + PER / 2>();   // slice 0 in LDS
             lds_barrier();
             if constexpr (NB > 0) static_for<0, NB + NJ>([&](auto r_c) { read_one<NB, decltype(r_c)::value>(f0, sm.ring.a[0], sm.ring.b[0], 0, r0w, c0w); });
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): exact wait counts at the loop head
             for (int kt = 0; kt + 1 < nk; ++kt) {
                 const int slot = kt % STAGES, ns = (kt + 1) % STAGES;
                 phase(nb_c, std::integral_constant<int, 2>{}, f0, f1, sm.ring.a[slot], sm.ring.b[slot], 1, kt + STAGES - 1);

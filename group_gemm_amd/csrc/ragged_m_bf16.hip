@@ -320,6 +320,7 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
             lds_barrier();
             if constexpr (NB > 0)
                 static_for<0, NB + NJ>([&](auto r_c) { read_one<MI, NJ, NB, decltype(r_c)::value, B_NK>(f0, sm.ring.a[0], sm.ring.b[0], 0, 0, r0w, c0w); });
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): exact wait counts at the loop head
             // iteration kt with P = kt % 2 fixed at compile time (A chunk offsets and A block
             // numbers depend on it)
             auto iter = [&](auto par_c, int kt) {
