@@ -29,7 +29,9 @@ __device__ inline i32x4 make_rsrc_v(const void* base, uint32_t bytes) {
     r[3] = kRsrcWord3;
     return r;
 }
-__device__ inline void bstore(rsrc_t r, uint32_t off, i32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0); }
+// output stores carry the nontemporal hint (cache-policy bit 1, `nt`): each output line is written
+// once and never read back by the kernel, so it need not displace operand panels in L2
+__device__ inline void bstore(rsrc_t r, uint32_t off, i32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 2); }
 // two floats -> two bf16 (round to nearest even), low element in the low half
 __device__ inline uint32_t pack_bf16(float a, float b) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
