@@ -47,10 +47,12 @@ constexpr int BSLICE = BK * BN;          // elements of one B slice: 16 KiB
 __device__ inline int b_swz(int kr) { return ((kr & 3) | (((kr >> 3) & 1) << 2)) << 2; }
 __device__ inline int b_off(int kr, int nn) { return kr * BN + (((nn >> 3) ^ b_swz(kr)) << 3) + (nn & 7); }
 // [rows][32 k] slice, 64-byte rows (the [n][k] weights of the data-gradient form): 16-byte
-// chunk XOR (row >> 1) & 3.  Measured on gfx950 with the fragment reads below (32
-// consecutive rows, one chunk per lane half), this swizzle runs ds_read_b128 at ~115 B/clk
-// per CU against ~76 for an XOR by (row >> 2) & 3.
-__device__ inline int a_off(int r, int chunk) { return r * BK + ((chunk ^ ((r >> 1) & 3)) << 3); }
+// chunk XOR (row >> 2) & 3.  The LDS serves a 16-byte-per-lane read 16 lanes at a time over
+// its 64 banks; the fragment reads below give those 16 lanes 16 consecutive rows and one
+// logical chunk, so the row's position in its 256-byte bank period (row & 3) and the XOR
+// ((row >> 2) & 3) together place them on all 64 banks once (rocprofv3 SQ_LDS_BANK_CONFLICT:
+// zero, against 0.5 conflict cycles per access with an XOR by (row >> 1) & 3).
+__device__ inline int a_off(int r, int chunk) { return r * BK + ((chunk ^ ((r >> 2) & 3)) << 3); }
 // A pair [BM rows][64 k] (two k slices), 128-byte rows: 16-byte chunk XOR (row >> 1) & 7, so
 // the 16 rows a quarter of a fragment read touches fill the 64 banks once.  The A ring holds
 // pairs because a load of 128 contiguous bytes per row moves twice the data per row as one of
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
     // B slice [32 k][256 n]: 1 KiB blocks of 2 rows, wave w fills blocks B_LOADS w + u; lane
     // l writes physical chunk l % 32 of row 2 b + l / 32, which holds logical chunk
     // (l & 31) ^ b_swz.  [n][k] weights (B_NK): 1 KiB blocks of 16 rows x 64 B; lane l writes
-    // physical chunk l % 4 of row 16 b + l / 4, logical chunk (l & 3) ^ ((row >> 1) & 3).
+    // physical chunk l % 4 of row 16 b + l / 4, logical chunk (l & 3) ^ ((row >> 2) & 3).
     int ap_ch[2];
     uint32_t ap_lane[2];
 #pragma unroll
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
         ap_ch[e] = (l & 7) ^ ((4 * e + (l >> 4)) & 7);
         ap_lane[e] = (uint32_t)(l >> 3) * k2 + (uint32_t)ap_ch[e] * 16u;
     }
-    const int nk_chunk = (l & 3) ^ ((l >> 3) & 3);
+    const int nk_chunk = (l & 3) ^ ((l >> 4) & 3);
     const uint32_t nk_lane = (uint32_t)(l >> 2) * k2 + (uint32_t)nk_chunk * 16u;
     // this wave's first 1 KiB block in A / B slot 0 (wave-uniform, scalar registers)
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);

@@ -42,8 +42,9 @@ struct Smem {
     Tables tab;
 };
 
-// A slice [256 rows][32 k], 64-byte rows: 16-byte chunk XOR (row >> 1) & 3 (the plain kernel's)
-__device__ inline int a_off(int r, int chunk) { return r * BK + ((chunk ^ ((r >> 1) & 3)) << 3); }
+// A slice [256 rows][32 k], 64-byte rows: 16-byte chunk XOR (row >> 2) & 3 (the plain kernel's
+// [n][k] weight layout: 16 consecutive rows of one chunk cover the 64 LDS banks once)
+__device__ inline int a_off(int r, int chunk) { return r * BK + ((chunk ^ ((r >> 2) & 3)) << 3); }
 // weight sub-slice [32 k][128 n], 256-byte rows: 16-byte chunk XOR 4 (k & 3), so the 4 rows
 // of one transpose read land in different 64-byte quarters of the banks
 __device__ inline int w_off(int kr, int nn) { return kr * ON + (((nn >> 3) ^ ((kr & 3) << 2)) << 3) + (nn & 7); }
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(GParams p) {
     // (u = 2, 3, u' = u - 2); lane l writes physical chunk l % 16 of row 4 b + l / 16,
     // which holds logical chunk (l & 15) ^ 4 ((l >> 4) & 3).
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const int a_chunk = (l & 3) ^ ((l >> 3) & 3);
+    const int a_chunk = (l & 3) ^ ((l >> 4) & 3);
     const uint32_t a_lane = (uint32_t)(l >> 2) * k2 + (uint32_t)a_chunk * 16u;
     const int w_ch8 = 8 * ((l & 15) ^ (((l >> 4) & 3) << 2));
     const uint32_t w_lane = (uint32_t)(l >> 4) * n2 + (uint32_t)w_ch8 * 2u;

@@ -60,9 +60,9 @@ struct Smem {
     Tables tab;
 };
 
-// A slot [256 rows][64 k bytes]: 16-byte chunk XOR (row >> 1) & 3 (the bf16 kernel's A
-// layout, byte for byte: 32 consecutive rows, one chunk per lane half, no bank conflicts).
-__device__ inline int a_off(int r, int chunk) { return r * BK + ((chunk ^ ((r >> 1) & 3)) << 4); }
+// A slot [256 rows][64 k bytes]: 16-byte chunk XOR (row >> 2) & 3 (the bf16 kernel's [n][k]
+// weight layout, byte for byte: 16 consecutive rows of one chunk cover the 64 LDS banks once).
+__device__ inline int a_off(int r, int chunk) { return r * BK + ((chunk ^ ((r >> 2) & 3)) << 4); }
 // B slot [64 k][256 n bytes]: 16-byte chunks XOR'ed by 2 (k & 7), so the 8 k rows one
 // 8-byte transpose read gathers fall in different bank groups.
 __device__ inline int b_off(int kr, int nn) { return kr * BN + ((((nn >> 4) ^ ((kr & 7) << 1))) << 4) + (nn & 15); }
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
 
     // per-lane parts of the ring-load offsets
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const int a_chunk = (l & 3) ^ ((l >> 3) & 3);   // A: row 16 b + l / 4 holds chunk (l & 3) ^ ((row >> 1) & 3)
+    const int a_chunk = (l & 3) ^ ((l >> 4) & 3);   // A: row 16 b + l / 4 holds chunk (l & 3) ^ ((row >> 2) & 3)
     const uint32_t a_lane = (uint32_t)(l >> 2) * (uint32_t)p.k + (uint32_t)a_chunk * 16u;
     uint32_t b_lane[4];
     int b_col[4];
