@@ -187,7 +187,7 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
     // tile walk: per-XCD queues when the launcher provides them (see ring.hpp)
     const bool queued = queued_walk(p.tile_queue);
     for (int tile = first_tile(queued);; tile += gridDim.x) {
-        if (queued) tile = queue_next(p.tile_queue, &sm.next_tile);
+        if (queued) tile = queue_next(p.tile_queue, &sm.next_tile, total);
         if (tile >= total) break;
         if (tile >= gemm_tiles) {   // rows past the covered ones: zeros
             const int z = tile - gemm_tiles;

@@ -109,13 +109,23 @@ __device__ inline void with_nb(int nb, F&& fn) {
 constexpr int kQueueChunk = 8;
 __device__ inline bool queued_walk(const int* queues) { return queues != nullptr && (gridDim.x & 7) == 0; }
 __device__ inline int first_tile(bool queued) { return queued ? 0 : xcd_virtual_id(blockIdx.x, gridDim.x); }
-// the next tile of a queued walk; `slot` is an int in LDS
-__device__ inline int queue_next(int* queues, int* slot) {
+// The next tile of a queued walk (>= total once every queue is empty); `slot` is an int in
+// LDS.  A workgroup whose own XCD's queue is empty takes the next tile of another XCD's queue,
+// so an XCD that runs at a lower clock does not hold up the end of the call: counter value c
+// of queue x is tile ((c / kQueueChunk) * 8 + x) * kQueueChunk + c % kQueueChunk, increasing
+// in c, so every tile is handed out exactly once and a queue, once past the last tile, stays
+// past it (the extra increments only move its counter further).
+__device__ inline int queue_next(int* queues, int* slot, int total) {
     __syncthreads();   // every thread has read the previous index
     if (threadIdx.x == 0) {
         const int xcd = blockIdx.x & 7;
-        const int c = atomicAdd(queues + xcd, 1);
-        *slot = ((c / kQueueChunk) * 8 + xcd) * kQueueChunk + c % kQueueChunk;
+        int tile = total;
+        for (int o = 0; o < 8 && tile >= total; ++o) {   // own queue first, then the others
+            const int x = (xcd + o) & 7;
+            const int c = atomicAdd(queues + x, 1);
+            tile = ((c / kQueueChunk) * 8 + x) * kQueueChunk + c % kQueueChunk;
+        }
+        *slot = tile;
     }
     __syncthreads();
     return *slot;
