@@ -100,10 +100,11 @@ __device__ inline void with_nb(int nb, F&& fn) {
 // Tile walk of the persistent ring kernels.  With queues (8 device ints, one per XCD,
 // zeroed by launch_clear_queues before the launch): the tiles are dealt to the 8 XCDs in
 // chunks of kQueueChunk consecutive tiles (chunk c to XCD c % 8; workgroup w runs on XCD
-// w % 8) and every workgroup takes its XCD's next tile from an atomic counter.  A chunk's
-// tiles share a row or weight panel and run side by side on one XCD, and workgroups that
-// drew cheap tiles (a short group, a group's partly filled last m-tile) take more, where
-// the static walk hands every workgroup the same number of tiles whatever they cost.
+// w % 8) and every workgroup takes its XCD's next tile from an atomic counter (another XCD's
+// once its own are gone).  A chunk's tiles share a row or weight panel and run side by side
+// on one XCD, and workgroups that drew cheap tiles (a short group, a group's partly filled
+// last m-tile) take more, where the static walk hands every workgroup the same number of
+// tiles whatever they cost.
 // Without queues, or with a grid that is not a multiple of 8: a static round-robin over
 // virtual ids that keeps consecutive tiles on one XCD.  All threads call these together.
 constexpr int kQueueChunk = 8;
