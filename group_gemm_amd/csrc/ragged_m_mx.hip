@@ -171,20 +171,25 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
 
         // ring load number d of k slice `stage` (A 0-3, B 4-7, row scales 8, column
         // scales 9); slices past k are zero-filled into the slot no one reads
-        auto dma_one = [&](auto d_c, int stage) {
+        auto dma_one = [&](auto d_c, int stage, auto full_c) {
             constexpr int d = decltype(d_c)::value;
+            // FULL: the slice lies inside k, so the checks below always pass for A and the row
+            // scales; B and column-scale loads past n (the last n-tile of a ragged n) then read
+            // the next row's bytes, or zeros past the buffer, which only reach output columns that
+            // are never stored
+            constexpr bool FULL = decltype(full_c)::value;
             const int kk = stage * BK;
             const uint32_t slot = lds0 + (uint32_t)(stage % STAGES) * SLOT;
             const bool live = stage < nk;
             if constexpr (d < 4) {
                 const bool ok = live && kk + 16 * a_chunk < p.k;
                 const uint32_t wpart = (uint32_t)(16 * (4 * wave_u + d)) * (uint32_t)p.k + (uint32_t)kk;
-                load_lds16(ra, slot + (uint32_t)(4 * wave_u + d) * 1024u, ok ? a_lane + wpart : kOOB);
+                load_lds16(ra, slot + (uint32_t)(4 * wave_u + d) * 1024u, FULL ? a_lane + wpart : (ok ? a_lane + wpart : kOOB));
             } else if constexpr (d < 8) {
                 constexpr int u = d - 4;
                 const bool ok = live && b_col[u] < p.n - col0;
                 const uint32_t wpart = (uint32_t)(kk + 4 * (4 * wave_u + u)) * (uint32_t)p.n + (uint32_t)col0;
-                load_lds16(rb, slot + OFF_B + (uint32_t)(4 * wave_u + u) * 1024u, ok ? b_lane[u] + wpart : kOOB);
+                load_lds16(rb, slot + OFF_B + (uint32_t)(4 * wave_u + u) * 1024u, FULL ? b_lane[u] + wpart : (ok ? b_lane[u] + wpart : kOOB));
             } else if constexpr (d == 8 && AS8) {
                 // rows 64 wave + l: the 16 scale bytes of k blocks 16 (stage / 8) .. + 15 with
                 // the block's first slice, a placeholder load with the others
@@ -195,12 +200,12 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
             } else if constexpr (d == 8) {
                 // rows 64 wave + l: the 4 scale bytes of k blocks 4 (stage / 2) .. + 3
                 const uint32_t off = (uint32_t)(64 * wave_u + l) * (uint32_t)kb + (uint32_t)(4 * (stage >> 1));
-                load_lds4(rsa, slot + OFF_AS + (uint32_t)wave_u * 256u, live ? off : kOOB);
+                load_lds4(rsa, slot + OFF_AS + (uint32_t)wave_u * 256u, FULL || live ? off : kOOB);
             } else {
                 // k-block row 2 stage + (wave & 1), columns col0 + 4 l .. + 3, into copy wave / 2
                 const bool ok = live && 4 * l < p.n - col0;
                 const uint32_t off = (uint32_t)(2 * stage + (wave_u & 1)) * (uint32_t)p.n + (uint32_t)(col0 + 4 * l);
-                load_lds4(rsb, slot + OFF_BS + (uint32_t)((wave_u >> 1) * 2 * BN + (wave_u & 1) * BN), ok ? off : kOOB);
+                load_lds4(rsb, slot + OFF_BS + (uint32_t)((wave_u >> 1) * 2 * BN + (wave_u & 1) * BN), FULL ? off : (ok ? off : kOOB));
             }
         };
 
@@ -225,8 +230,9 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
             // iteration's barrier has passed), the rest in phase 1 of iteration s - 3, so the
             // loads are spread over all the slice's MFMAs.  Either way PER * (STAGES - 2)
             // loads are issued after slice kt + 1's last one by the time iteration kt waits.
-            static_for<0, STAGES - 1>([&](auto st_c) { static_for<0, PER>([&](auto d_c) { dma_one(d_c, decltype(st_c)::value); }); });
-            static_for<0, PER / 2>([&](auto d_c) { dma_one(d_c, STAGES - 1); });
+            constexpr std::false_type chk{};
+            static_for<0, STAGES - 1>([&](auto st_c) { static_for<0, PER>([&](auto d_c) { dma_one(d_c, decltype(st_c)::value, chk); }); });
+            static_for<0, PER / 2>([&](auto d_c) { dma_one(d_c, STAGES - 1, chk); });
             wait_vm<PER * (STAGES - 2) + PER / 2>();   // slice 0 in LDS
             lds_barrier();
             if constexpr (NB > 0) {
@@ -240,7 +246,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
             __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
             // phase 1 of slice kt: MFMAs (i, 0..1), the second half of the ring loads of slice
             // `stage` (when DMA), reads of B blocks 2, 3 of slot kt
-            auto phase1 = [&](auto dma_c, const Slot& s, int stage) {
+            auto phase1 = [&](auto dma_c, const Slot& s, int stage, auto full_c) {
                 constexpr bool DMA = decltype(dma_c)::value;
                 constexpr int NM = 2 * NB, ND = DMA ? PER - PER / 2 : 0, NR = NB > 0 ? 2 : 0;
                 constexpr int NOPS = ND + NR;
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
                         else {
                             constexpr int d = o - (NR > 0 ? (o > RB3 ? 2 : (o > RB2 ? 1 : 0)) : 0);
                             static_assert(d >= 0 && d < ND, "op index");
-                            dma_one(std::integral_constant<int, PER / 2 + d>{}, stage);
+                            dma_one(std::integral_constant<int, PER / 2 + d>{}, stage, full_c);
                         }
                     });
                     __builtin_amdgcn_sched_barrier(0);
@@ -268,7 +274,7 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
             // phase 2 of slice kt: MFMAs (i, 2..3), reads of slot kt + 1 (A block i after its
             // last MFMA, B blocks 0, 1 spread over the first MFMAs) when NEXT, and the first half
             // of the ring loads of slice `stage`, spread over the MFMAs
-            auto phase2 = [&](auto next_c, const Slot& s, int ks1, int stage) {
+            auto phase2 = [&](auto next_c, const Slot& s, int ks1, int stage, auto full_c) {
                 constexpr bool NEXT = decltype(next_c)::value;
                 constexpr int NM = 2 * NB, ND = NEXT ? PER / 2 : 0;
                 static_for<0, NM>([&](auto m_c) {
@@ -282,21 +288,27 @@ __global__ __launch_bounds__(NT, 1) void kernel(MParams p) {
                         static_for<0, ND>([&](auto q_c) {
                             constexpr int q = decltype(q_c)::value;
                             constexpr int at = q * NM / ND;
-                            if constexpr (at == m) dma_one(q_c, stage);
+                            if constexpr (at == m) dma_one(q_c, stage, full_c);
                         });
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 });
-                if constexpr (NM == 0 && NEXT) static_for<0, ND>([&](auto q_c) { dma_one(q_c, stage); });
+                if constexpr (NM == 0 && NEXT) static_for<0, ND>([&](auto q_c) { dma_one(q_c, stage, full_c); });
             };
-            for (int kt = 0; kt + 1 < nk; ++kt) {
-                phase1(std::true_type{}, sm.ring[kt % STAGES], kt + STAGES - 1);
+            auto iter = [&](int kt, auto full_c) {
+                phase1(std::true_type{}, sm.ring[kt % STAGES], kt + STAGES - 1, full_c);
                 wait_vm<PER * (STAGES - 2)>();   // slice kt + 1 in LDS
                 lds_barrier();
-                phase2(std::true_type{}, sm.ring[(kt + 1) % STAGES], kt + 1, kt + STAGES);
-            }
-            phase1(std::false_type{}, sm.ring[(nk - 1) % STAGES], 0);
-            phase2(std::false_type{}, sm.ring[0], 0, 0);
+                phase2(std::true_type{}, sm.ring[(kt + 1) % STAGES], kt + 1, kt + STAGES, full_c);
+            };
+            int kt = 0;
+            // Iterations whose ring loads all fall inside k skip the range checks (one select and
+            // its condition per load: 175 instead of 190 instructions per slice; 2-3 % faster,
+            // results bit-identical); the last ones keep them.
+            for (; kt + STAGES < nk; ++kt) iter(kt, std::true_type{});
+            for (; kt + 1 < nk; ++kt) iter(kt, chk);
+            phase1(std::false_type{}, sm.ring[(nk - 1) % STAGES], 0, chk);
+            phase2(std::false_type{}, sm.ring[0], 0, 0, chk);
         };
         if (nk > 0) with_nb<MI>(nb, run);
         // Every ring load has landed (the zero-fill loads of slices past the end may still be
