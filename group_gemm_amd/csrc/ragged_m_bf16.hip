@@ -253,10 +253,11 @@ __global__ __launch_bounds__(64 * NW, 1) void kernel(MParams p) {
                 const uint32_t wpart = (uint32_t)(col0 + 16 * (C::B_LOADS * wave_u + u)) * k2 + (uint32_t)kk * 2u;
                 load(dst, ok ? nk_lane + wpart : kOOB);
             } else {
-                // k row kk + 2 (4 wave + u) + l / 32, columns col0 + b_ch8 .. + 7
-                const bool ok = kk < p.k && b_ch8[u] < p.n - col0;
+                // k row kk + 2 (4 wave + u) + l / 32, columns col0 + b_ch8 .. + 7.  Unchecked: rows
+                // past k lie past the descriptor's end and read zeros, and columns past n read
+                // other weights that reach only output columns that are never stored.
                 const uint32_t wpart = (uint32_t)(kk + 2 * (C::B_LOADS * wave_u + u)) * n2 + (uint32_t)col0 * 2u;
-                load(dst, ok ? b_lane[u] + wpart : kOOB);
+                load(dst, b_lane[u] + wpart);
             }
         };
 
