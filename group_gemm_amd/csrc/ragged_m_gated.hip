@@ -133,19 +133,19 @@ __global__ __launch_bounds__(NT, 1) void kernel(GParams p) {
         // the caller knows it)
         auto dma_one = [&](auto d_c, int stage, int slot) {
             constexpr int d = decltype(d_c)::value;
-            const int kk = stage * BK;
-            const bool live = stage < nk;
+            const int kk = __builtin_amdgcn_readfirstlane(stage * BK);
             if constexpr (d < 4) {
-                const bool ok = live && kk + 8 * a_chunk < p.k;
+                const bool ok = kk + 8 * a_chunk < p.k;
                 const uint32_t wpart = (uint32_t)(16 * (4 * wave_u + d)) * k2 + (uint32_t)kk * 2u;
                 load_lds16(ra, lds_a + (uint32_t)slot * (ASLICE * 2) + d * 1024u, ok ? a_lane + wpart : kOOB);
             } else {
                 constexpr int u = d - 4, mat = u >> 1, up = u & 1;
                 const int row = 4 * (2 * wave_u + up);   // first of this block's 4 k rows
-                const bool ok = live && w_ch8 < p.n - col0;
+                // unchecked: k rows past the end lie past the descriptor's end and read zeros, and
+                // columns past n read other weights, which reach only output columns never stored
                 const uint32_t wpart = (uint32_t)(kk + row) * n2 + (uint32_t)col0 * 2u;
                 const uint32_t dst = lds_w + (uint32_t)(slot * 2 + mat) * (WSLICE * 2) + (uint32_t)(row >> 2) * 1024u;
-                load_lds16(mat ? rw1 : rw0, dst, ok ? w_lane + wpart : kOOB);
+                load_lds16(mat ? rw1 : rw0, dst, w_lane + wpart);
             }
         };
 
