@@ -449,6 +449,38 @@ def test_ragged_m_gated_random_shapes(i):
     assert torch.all(y[int(gs.sum()):] == 0)
 
 
+@pytest.mark.parametrize("op", ["m", "gated"])
+def test_weights_out_of_range_never_reach_stored_outputs(op):
+    """Weight ring loads run unchecked: k rows past a group's end must fall past its
+    descriptor (read as zeros) and columns past n may only feed output columns that are never
+    stored.  Non-finite weights where only such loads could reach them -- the whole slab of an
+    empty group, and column 0 of every k row but the first, which the wrapped columns past n
+    of the previous row read -- must leave the stored outputs equal to the oracle's (k = 72
+    ends inside a k slice, n = 200 inside an output tile; column 0 itself is not compared)."""
+    m, k, n, gs = 320, 72, 200, [100, 0, 120, 80]
+    say("out-of-range weights", op, m, k, n, gs)
+    d = W.small_inputs("m", "bf16", m, k, n, gs, seed=811)
+    ws = [d["rhs"]] + ([W.small_inputs("m", "bf16", m, k, n, gs, seed=812)["rhs"]] if op == "gated" else [])
+    for w in ws:
+        w[1] = float("inf")
+        w[:, 1:, 0] = float("inf")
+    with np.errstate(invalid="ignore", over="ignore"):
+        if op == "m":
+            ref = oracle.ragged_dot_m(raw(d["lhs"]), raw(ws[0]), np.asarray(gs, np.int32))
+        else:
+            ref = oracle.ragged_dot_m_gated(raw(d["lhs"]), raw(ws[0]), raw(ws[1]), np.asarray(gs, np.int32), act="silu")
+    d = to_dev(d)
+    ws = [w.to(DEV) for w in ws]
+    out = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    if op == "m":
+        y = gg().ragged_dot_m(d["lhs"], ws[0], d["group_sizes"], out=out)
+    else:
+        y = gg().ragged_dot_m_gated(d["lhs"], ws[0], ws[1], d["group_sizes"], act="silu", out=out)
+    torch.cuda.synchronize()
+    check_bf16(y[:, 1:], ref[:, 1:], f"out-of-range weights ({op})")
+    assert torch.all(y[sum(gs):] == 0)
+
+
 # ---- fused gate/up projection: act(x . w0 + b0) * (x . w1 + b1) ------------------------------
 
 GATED_CASES = [
