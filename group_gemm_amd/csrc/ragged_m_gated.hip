@@ -133,6 +133,10 @@ __global__ __launch_bounds__(NT, 1) void kernel(GParams p) {
         // the caller knows it)
         auto dma_one = [&](auto d_c, int stage, int slot) {
             constexpr int d = decltype(d_c)::value;
+            // (the k offset goes through readfirstlane, opaque to loop strength reduction: left
+            // visible, the lane offsets become vector induction variables, one of them spilled,
+            // and its reload before the main loop made the loop wait for every ring load in
+            // flight once per four iterations)
             const int kk = __builtin_amdgcn_readfirstlane(stage * BK);
             if constexpr (d < 4) {
                 const bool ok = kk + 8 * a_chunk < p.k;

@@ -15,13 +15,14 @@ import pytest
 
 from group_gemm_amd import build as B
 
-# name: (source, mangled-name prefix of the instantiation, most instructions per MFMA allowed)
+# name: (source, mangled-name prefix of the instantiation, most instructions per MFMA allowed,
+#        most scratch bytes per lane: spilled registers, whose reloads wait for every load in flight)
 LOOPS = {
-    "bf16 forward": ("ragged_m_bf16.hip", "_ZN2gg2mb6kernelILi256ELi2ELi3ELi4ELb0ELb0EtEE", 3.5),
-    "bf16 data gradient": ("ragged_m_bf16.hip", "_ZN2gg2mb6kernelILi256ELi2ELi3ELi4ELb1ELb0EtEE", 3.4),
-    "MXFP8 forward": ("ragged_m_mx.hip", "_ZN2gg2mx6kernelILb1ELb0EtEE", 11.5),
-    "weight gradient": ("ragged_k_bf16.hip", "_ZN2gg2kr6kernelILb0EfLb0EEE", 5.5),
-    "gated": ("ragged_m_gated.hip", "_ZN2gg2mg6kernelILi0EtEE", 3.5),
+    "bf16 forward": ("ragged_m_bf16.hip", "_ZN2gg2mb6kernelILi256ELi2ELi3ELi4ELb0ELb0EtEE", 3.55, 128),
+    "bf16 data gradient": ("ragged_m_bf16.hip", "_ZN2gg2mb6kernelILi256ELi2ELi3ELi4ELb1ELb0EtEE", 3.4, 64),
+    "MXFP8 forward": ("ragged_m_mx.hip", "_ZN2gg2mx6kernelILb1ELb0EtEE", 11.5, 0),
+    "weight gradient": ("ragged_k_bf16.hip", "_ZN2gg2kr6kernelILb0EfLb0EEE", 5.5, 0),
+    "gated": ("ragged_m_gated.hip", "_ZN2gg2mg6kernelILi0EtEE", 3.5, 0),
 }
 
 
@@ -68,7 +69,7 @@ def innermost_loops(text, prefix):
 
 @pytest.mark.parametrize("name", list(LOOPS))
 def test_main_loop_budget(asm, name):
-    src, prefix, budget = LOOPS[name]
+    src, prefix, budget, scratch = LOOPS[name]
     loops = innermost_loops(asm[src], prefix)
     assert loops, f"{name}: no loop found"
     nm = lambda ins: sum(1 for x in ins if x.startswith("v_mfma"))
@@ -80,3 +81,6 @@ def test_main_loop_budget(asm, name):
     assert ratio <= budget, f"{name}: {len(ins)} instructions for {top} MFMAs ({ratio:.2f} per MFMA) in {label}"
     assert not any(x.startswith("scratch_") for x in ins), f"{name}: spill traffic in the main loop {label}"
     assert not any(re.match(r"s_waitcnt\s+vmcnt\(0\)", x) for x in ins), f"{name}: vmcnt(0) in the main loop {label}"
+    m = re.search(r"^" + prefix + r"\w*:", asm[src], re.M)
+    size = re.search(r"; ScratchSize: (\d+)", asm[src][asm[src].index(".Lfunc_end", m.start()):])
+    assert size and int(size.group(1)) <= scratch, f"{name}: {size and size.group(1)} scratch bytes per lane"
