@@ -20,8 +20,8 @@ from group_gemm_amd import build as B
 LOOPS = {
     "bf16 forward": ("ragged_m_bf16.hip", "_ZN2gg2mb6kernelILi256ELi2ELi3ELi4ELb0ELb0EtEE", 3.55, 128),
     "bf16 data gradient": ("ragged_m_bf16.hip", "_ZN2gg2mb6kernelILi256ELi2ELi3ELi4ELb1ELb0EtEE", 3.4, 64),
-    "MXFP8 forward": ("ragged_m_mx.hip", "_ZN2gg2mx6kernelILb1ELb0EtEE", 11.5, 0),
-    "weight gradient": ("ragged_k_bf16.hip", "_ZN2gg2kr6kernelILb0EfLb0EEE", 5.5, 0),
+    "MXFP8 forward": ("ragged_m_mx.hip", "_ZN2gg2mx6kernelILb1ELb0EtEE", 8.5, 64),
+    "weight gradient": ("ragged_k_bf16.hip", "_ZN2gg2kr6kernelILb0EfLb0EEE", 3.8, 0),
     "gated": ("ragged_m_gated.hip", "_ZN2gg2mg6kernelILi0EtEE", 3.5, 0),
 }
 
