@@ -110,8 +110,9 @@ __device__ long long block_exclusive_scan(long long v, Tables& T, long long* tot
 // Builds row_off / tile_off for `g` groups into T, where a group of s rows contributes
 // ceil(s / block_m) * tiles_per_mtile tiles (tiles_per_mtile may be 0 for "rows only").
 // Returns (via refs) the number of GEMM tiles and the rows covered; T.flags gets GG_DEV_*.
+// (Forced inline: the larger ring kernels otherwise call it out of line.)
 template <int NT>
-__device__ void build_tables(const int32_t* __restrict__ group_sizes, int g, long long m,
+__device__ __attribute__((always_inline)) inline void build_tables(const int32_t* __restrict__ group_sizes, int g, long long m,
                              int block_m, int tiles_per_mtile, Tables& T, int* n_tiles,
                              int* covered) {
     constexpr int PER = (GG_MAX_GROUPS + NT - 1) / NT;

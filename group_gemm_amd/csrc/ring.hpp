@@ -86,9 +86,10 @@ __device__ inline void static_for(F&& f) {
         static_for<B + 1, E>(f);
     }
 }
-// calls fn(std::integral_constant<int, NB>) for the runtime value nb in [0, MAX]
+// calls fn(std::integral_constant<int, NB>) for the runtime value nb in [0, MAX] (forced inline:
+// kept out of line, the per-NB bodies would pass their fragment registers through memory)
 template <int MAX, typename F>
-__device__ inline void with_nb(int nb, F&& fn) {
+__device__ __attribute__((always_inline)) inline void with_nb(int nb, F&& fn) {
     if constexpr (MAX > 0) {
         if (nb >= MAX) { fn(std::integral_constant<int, MAX>{}); return; }
         with_nb<MAX - 1>(nb, fn);
